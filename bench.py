@@ -1,0 +1,207 @@
+"""Benchmark of the deterministic attention backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+One step = one dash_attn_bwd call (preprocess + persistent backward, plus the
+finalize pass for the atomic reference) over one batch of synthetic bf16 input
+already resident in HBM.  Each schedule is timed separately: W untimed calls,
+then K calls between two device synchronisations, with HIP events recorded on
+the call's stream around every call.  Prints one JSON line.
+
+The headline value is the throughput of the fastest deterministic schedule in
+TFLOP/s with FLOPs = 10*B*Hq*S^2*D (halved for a causal mask).  The roofline
+object prices the persistent backward kernel against the bf16 dense MFMA peak.
+The cpu_baseline object times the float64 oracle on a bounded sample of the
+same workload on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+CONFIGS = {
+    "llama8b_causal": dict(B=4, S=4096, Hq=32, Hkv=8, D=128, causal=True,
+                           desc="causal attention backward shaped like an 8B Llama-style "
+                                "layer: B=4 S=4096 Hq=32 Hkv=8 (GQA 4) D=128"),
+    "small_full": dict(B=1, S=256, Hq=2, Hkv=2, D=64, causal=False,
+                       desc="full-mask attention backward B=1 S=256 Hq=Hkv=2 D=64"),
+    "dit_full": dict(B=2, S=4096, Hq=24, Hkv=24, D=64, causal=False,
+                     desc="full-mask attention backward shaped like a diffusion/vision "
+                          "block: B=2 S=4096 Hq=Hkv=24 D=64"),
+    "long_full": dict(B=1, S=16384, Hq=32, Hkv=32, D=128, causal=False,
+                      desc="long-sequence full-mask attention backward B=1 S=16384 "
+                           "Hq=Hkv=32 D=128"),
+    "qwen7b_causal": dict(B=1, S=16384, Hq=28, Hkv=4, D=128, causal=True,
+                          desc="long-sequence causal attention backward shaped like a 7B "
+                               "Qwen-style layer: B=1 S=16384 Hq=28 Hkv=4 (GQA 7) D=128"),
+}
+DEFAULT_CONFIG = "llama8b_causal"
+
+
+def flops(cfg):
+    f = 10.0 * cfg["B"] * cfg["Hq"] * cfg["S"] ** 2 * cfg["D"]
+    return f / 2 if cfg["causal"] else f
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
+    import torch
+    mask = 1 if cfg["causal"] else 0
+    ws = dash.new_workspace(x["q"], x["k"], mask, sched)
+    dq = torch.empty_like(x["q"])
+    dk = torch.empty_like(x["k"])
+    dv = torch.empty_like(x["v"])
+    stream = torch.cuda.current_stream()
+
+    def call():
+        dash.dash_attn_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, dq, dk, dv,
+                           mask, sched, ws, stream)
+
+    for _ in range(warmup):
+        call()
+    dash.dash_attn_bwd_check(ws, stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for n in range(steps):
+        starts[n].record(stream)
+        call()
+        ends[n].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dash.dash_attn_bwd_check(ws, stream)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean_ms = sum(per) / len(per)
+    return {"ms_mean": mean_ms, "ms_median": per[len(per) // 2], "ms_p10": per[len(per) // 10],
+            "ms_p90": per[min(len(per) - 1, (9 * len(per)) // 10)],
+            "wall_ms_per_step": 1e3 * wall / steps}
+
+
+def cpu_baseline(cfg, budget_s=20.0):
+    """Time the float64 oracle on whole (batch 0, kv head) groups until the
+    budget is used; report the rate in TFLOP/s of the same FLOP formula."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import attention as oa
+    from scheduling_persistent_attn_amd.inputs import as_float64, make_inputs
+
+    B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    G = Hq // Hkv
+    x = make_inputs(1, S, Hq, Hkv, D, seed=1000)
+    h = {k: as_float64(v) for k, v in x.items()}
+    t0 = time.perf_counter()
+    groups = 0
+    while True:
+        kv = groups % Hkv
+        hs = list(range(kv * G, (kv + 1) * G))
+        oa.attention_backward(h["q"][:, :, hs], h["k"][:, :, kv:kv + 1],
+                              h["v"][:, :, kv:kv + 1], h["do"][:, :, hs], cfg["causal"])
+        groups += 1
+        if time.perf_counter() - t0 >= budget_s or groups >= Hkv:
+            break
+    dt = time.perf_counter() - t0
+    fl = flops(dict(cfg, B=1, Hq=G * groups))
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, info.get("num_threads", 0))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": "float64 oracle forward+backward of %d of %d (batch, kv head) groups "
+                      "(%d query heads, batch 0) at S=%d D=%d, %.1f s; includes the oracle's "
+                      "own float64 forward" % (groups, B * Hkv, G * groups, S, D, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
+    ap.add_argument("--schedules", default="naive,descending_q,shift,symmetric_shift,atomic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import scheduling_persistent_attn_amd as dash
+    from scheduling_persistent_attn_amd.inputs import make_inputs
+
+    cfg = CONFIGS[args.config]
+    B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    x = make_inputs(B, S, Hq, Hkv, D, seed=1000, device="cuda")
+    o, lse = dash.forward(x["q"], x["k"], x["v"], cfg["causal"])
+    torch.cuda.synchronize()
+    fl = flops(cfg)
+
+    results = {}
+    for name in args.schedules.split(","):
+        sched = dash.SCHEDULES[name]
+        if sched == dash.SYMMETRIC_SHIFT and (not cfg["causal"] or N % 2):
+            continue
+        r = time_schedule(dash, x, o, lse, cfg, sched, args.steps, args.warmup)
+        r["tflops"] = fl / (r["ms_mean"] * 1e-3) / 1e12
+        r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
+        results[name] = r
+        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak" % (name, r["ms_mean"], r["tflops"],
+                                                               r["pct_peak"]))
+    det = {k: v for k, v in results.items() if k != "atomic"}
+    best = max(det, key=lambda k: det[k]["tflops"])
+    atomic = results.get("atomic")
+    for k, v in results.items():
+        v["det_over_atomic"] = (v["tflops"] / atomic["tflops"]) if atomic else None
+
+    bestr = det[best]
+    line = {
+        "metric": "deterministic attn-bwd TFLOP/s on 1 MI355X; % bf16 MFMA peak; ratio vs atomic dQ",
+        "value": round(bestr["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(bestr["ms_mean"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: N(0,1) fp32 cast to bf16, seeds 1000-1003; O and LSE from dash_attn_fwd",
+        "config": {"workload": cfg["desc"], "B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
+                   "mask": "causal" if cfg["causal"] else "full", "tile": T,
+                   "best_schedule": best},
+        "pct_peak": round(bestr["pct_peak"], 2),
+        "det_over_atomic": round(bestr["det_over_atomic"], 4) if atomic else None,
+        "schedules": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                          for kk, vv in v.items()} for k, v in results.items()},
+        "roofline": {
+            "bound": "mfma",
+            # algorithmic FLOPs of one call / mean event-timed duration of the
+            # call (preprocess + persistent kernel; the preprocess is ~1%)
+            "achieved": round(bestr["tflops"], 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bestr["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 6)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

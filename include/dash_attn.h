@@ -1,0 +1,203 @@
+/*
+ * dash_attn.h -- deterministic attention backward for AMD MI355X (gfx950).
+ *
+ * C ABI of libdash_attn.so.  Plain pointers and sizes only.
+ *
+ * The method: the softmax-attention backward computed tile by tile with the
+ * dK/dV of one key/value tile kept in registers while the unit walks that
+ * tile's query tiles (a "chain"), and with dQ accumulated across key/value
+ * tiles in a fixed order so that results are bitwise reproducible.  Sources:
+ * "DASH: Deterministic Attention Scheduling for High-throughput Reproducible
+ * LLM Training", explained on gist.science (technical summary in Spanish and
+ * Chinese, lay explanation in French); section numbers below refer to the
+ * technical summary.
+ *
+ * Tensor layouts (all device pointers, bf16 = IEEE bfloat16, row-major,
+ * contiguous, 16-byte aligned):
+ *   q, o, dout, dq : [B, S, Hq,  D] bf16
+ *   k, v, dk, dv   : [B, S, Hkv, D] bf16
+ *   lse            : [B, Hq, S]     fp32, natural-log log-sum-exp of the
+ *                                    scaled, masked scores of each query row
+ * Query head h reads key/value head h / (Hq / Hkv).  The softmax scale is
+ * 1/sqrt(D).  Causal masking hides key positions after the query position
+ * (equal query and key lengths).  Supported: D in {64, 128}; any S >= 0
+ * (the last tile may be partial); Hq a positive multiple of Hkv.
+ *
+ * Ownership: the caller owns every buffer, including the workspace (size from
+ * dash_attn_bwd_workspace_size).  The library allocates no device memory; it
+ * caches the device's compute-unit count and the kernels' occupancy.  Calls
+ * are asynchronous on the given HIP stream (NULL = default stream).
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * a non-zero status means nothing was launched.  A failed kernel launch
+ * returns DASH_ERR_HIP.  A device-side watchdog turns a stalled ordered
+ * reduction into an error flag in the workspace, reported by
+ * dash_attn_bwd_check as DASH_ERR_TIMEOUT (the outputs are then undefined).
+ */
+#ifndef DASH_ATTN_H
+#define DASH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dash_mask { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 };
+
+/* Tile schedules of the backward pass (technical summary, section 2.2).
+ *  NAIVE            each key/value chain walks its query tiles upward; every
+ *                   dQ tile is reduced in ascending key/value order (the rigid
+ *                   order of section 1 that the method improves on).
+ *  DESCENDING_Q     chains walk their query tiles from the last to the first
+ *                   (section 2.2 A); same reduction order as NAIVE.
+ *  SHIFT            chain i visits query tiles i, i+1, ..., N-1, 0, ..., i-1
+ *                   (section 2.2 B, full masks); every dQ tile is reduced in
+ *                   the order the chains reach it in lockstep.  With a causal
+ *                   mask the masked tiles of the cycle are skipped.
+ *  SYMMETRIC_SHIFT  causal masks with an even tile count: key/value tiles p
+ *                   and N-1-p share one unit; a dense phase over
+ *                   {KV < N/2} x {Q >= N/2}, then the two folded triangles
+ *                   (section 2.2 B, symmetric shift).
+ *  ATOMIC           NOT deterministic: dQ reduced with unordered fp32 atomic
+ *                   adds (the non-deterministic counterpart of section 1);
+ *                   kept only as the speed reference.
+ */
+enum dash_schedule {
+  DASH_SCHED_NAIVE = 0,
+  DASH_SCHED_DESCENDING_Q = 1,
+  DASH_SCHED_SHIFT = 2,
+  DASH_SCHED_SYMMETRIC_SHIFT = 3,
+  DASH_SCHED_ATOMIC = 4
+};
+
+enum dash_status {
+  DASH_OK = 0,
+  DASH_ERR_NULL = 1,          /* a required pointer is NULL                 */
+  DASH_ERR_SHAPE = 2,         /* negative size, Hq % Hkv != 0, misaligned    */
+  DASH_ERR_UNSUPPORTED = 3,   /* head dim, or a schedule that needs a whole
+                                 group of chains resident at once on more
+                                 units than the device runs concurrently    */
+  DASH_ERR_SCHEDULE_MASK = 4, /* unknown mask/schedule, or SYMMETRIC_SHIFT
+                                 with a full mask or an odd tile count       */
+  DASH_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required     */
+  DASH_ERR_HIP = 6,           /* a HIP runtime call or launch failed         */
+  DASH_ERR_TIMEOUT = 7        /* the device watchdog fired during a backward */
+};
+
+/* Query-tile and key/value-tile edge T used for a problem (both sides use the
+ * same T): 64 when D == 64 and S <= 512, else 128.  Returns 0 if D is
+ * unsupported. */
+int dash_attn_tile_size(int S, int D);
+
+/* Bytes of workspace dash_attn_bwd needs for these arguments, or 0 if the
+ * arguments are invalid.  Layout (offsets rounded up to 256 bytes):
+ *   ctrl      64 x int32   [0] work-dispatch counter, [1] watchdog flag,
+ *                          [2] number of waits that timed out
+ *   counters  B*Hq*N*W int32: the turn counter of every (batch, query head,
+ *             dQ tile, wave slice); after a deterministic backward each holds
+ *             the number of key/value tiles that reduced into that dQ tile
+ *             (N = ceil(S/T), W = T/32)
+ *   delta     B*Hq*N*T fp32: rowsum(dO * O), zero past S
+ *   lse2      B*Hq*N*T fp32: lse * log2(e), +inf past S
+ *   dqacc     B*Hq*N*T*D fp32: dQ partial sums in the kernels' lane order
+ */
+size_t dash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int S, int D,
+                                    int mask, int schedule);
+
+/* Attention forward (support for the backward): o = softmax(scale*q k^T +
+ * mask) v in bf16 (round to nearest even) and lse in fp32.  Overwrites o and
+ * lse.  Not part of the deterministic-reduction contract, but itself
+ * deterministic (no cross-workgroup reduction). */
+int dash_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int B, int Hq, int Hkv, int S, int D, int mask,
+                  void* stream);
+
+/* Attention backward: overwrites dq, dk, dv (bf16, round to nearest even)
+ * with the gradients of sum(dout * o) with respect to q, k, v, given the
+ * forward's o and lse.  Arithmetic: bf16 operands, fp32 accumulation; P and
+ * dS are rounded to bf16 before their products.
+ *
+ * Determinism contract (schedules 0-3): for fixed inputs, shape, mask,
+ * schedule and library binary, dq/dk/dv are bitwise identical across calls,
+ * streams and timing.  Different schedules may differ in the last bits.
+ * dK/dV of a key/value head are summed over its query heads in ascending
+ * order inside one unit.  The dQ tile j of query head h is reduced in the
+ * order given by the schedule (see enum dash_schedule) using per-tile turn
+ * counters in the workspace.
+ *
+ * The workspace must not be shared by concurrently running calls. */
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk,
+                  void* dv, int B, int Hq, int Hkv, int S, int D, int mask,
+                  int schedule, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Waits for the stream, then reports DASH_ERR_TIMEOUT if the watchdog of the
+ * last backward that used this workspace fired, DASH_ERR_HIP on a runtime
+ * error, else DASH_OK.  Reads 8 bytes of the workspace. */
+int dash_attn_bwd_check(const void* workspace, void* stream);
+
+/* Static description of a status code. */
+const char* dash_status_string(int status);
+
+/* Number of persistent workgroups the backward launches for these arguments
+ * (compute units x resident workgroups per unit), or 0 if invalid / no
+ * device.  Queries the current device. */
+int dash_attn_bwd_grid_size(int S, int D, int mask);
+
+/* ---------------------------------------------------------------------------
+ * Schedule description (host only; the kernels evaluate the same closed forms
+ * on the device).  One item is the unit of work a persistent workgroup takes:
+ * a key/value chain (NAIVE, DESCENDING_Q, SHIFT, ATOMIC) or a symmetric pair
+ * (SYMMETRIC_SHIFT), covering all G query heads of one key/value head.
+ */
+
+/* Items per (batch, key/value head) group, or -1 if invalid. */
+int dash_schedule_num_items(int mask, int schedule, int N);
+
+/* Tasks in item `item` of a group with G query heads per key/value head, or
+ * -1 if invalid. */
+int dash_schedule_item_len(int mask, int schedule, int N, int G, int item);
+
+/* Task `step` of item `item`: writes query head g (0..G-1), key/value tile i,
+ * query tile j and the rank of that reduction in dQ tile (g, j).  Returns 0,
+ * or -1 if out of range. */
+int dash_schedule_task(int mask, int schedule, int N, int G, int item,
+                       int step, int* g, int* i, int* j, int* rank);
+
+/* ---------------------------------------------------------------------------
+ * Schedule simulator (CPU).  Builds the backward DAG of the technical
+ * summary's section 2.1 for `groups` independent (batch, key/value head)
+ * groups of N x N tiles with G query heads each, placed on P workers, and
+ * reports its critical path and the depth condition of Lemma 1 (section 2.2
+ * B) on every added accumulation-order edge.
+ *
+ * Events per task: S, E (compute, weight c, or c_diag on a causal diagonal
+ * tile), R, F (reduction, weight r); zero-weight edges E->R, between
+ * consecutive tasks of an item, between consecutive items of a worker, and
+ * the order edges F(rank q) -> R(rank q+1) of every dQ tile.  depth = longest
+ * path from a source.  dispatch 0: item k runs on worker k mod P; 1: the next
+ * item goes to the first idle worker (lower index on ties), as on the GPU.
+ */
+typedef struct {
+  double makespan;      /* critical path of the full DAG (+inf on deadlock) */
+  double base_makespan; /* critical path without the order edges            */
+  double total_work;    /* sum of all compute and reduction weights         */
+  double efficiency;    /* total_work / (min(P, items) * makespan)          */
+  double max_deficit;   /* largest depth(u) - depth(v) over order edges     */
+  long long order_edges;
+  long long violations; /* order edges with depth(u) > depth(v)             */
+  int deadlock;         /* 1 if the order edges close a cycle or the replay
+                           stalls                                           */
+} dash_sim_result;
+
+int dash_sim_run(int mask, int schedule, int N, int G, int groups, int P,
+                 int dispatch, double c_full, double c_diag, double r,
+                 dash_sim_result* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_ATTN_H */

@@ -1,0 +1,233 @@
+"""Python binding of libdash_attn.so (deterministic attention backward, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  The names follow the C ABI in include/dash_attn.h.  PyTorch provides
+device memory and streams.  If the library is missing the binding raises; it
+has no fallback.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdash_attn.so")
+
+MASK_FULL, MASK_CAUSAL = 0, 1
+NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT, ATOMIC = 0, 1, 2, 3, 4
+SCHEDULES = {"naive": NAIVE, "descending_q": DESCENDING_Q, "shift": SHIFT,
+             "symmetric_shift": SYMMETRIC_SHIFT, "atomic": ATOMIC}
+DETERMINISTIC = (NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT)
+
+DASH_OK = 0
+DASH_ERR_NULL = 1
+DASH_ERR_SHAPE = 2
+DASH_ERR_UNSUPPORTED = 3
+DASH_ERR_SCHEDULE_MASK = 4
+DASH_ERR_WORKSPACE = 5
+DASH_ERR_HIP = 6
+DASH_ERR_TIMEOUT = 7
+
+SYMBOLS = (
+    "dash_attn_tile_size", "dash_attn_bwd_workspace_size", "dash_attn_fwd",
+    "dash_attn_bwd", "dash_attn_bwd_check", "dash_status_string",
+    "dash_attn_bwd_grid_size", "dash_schedule_num_items",
+    "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run",
+)
+
+
+class DashError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, dash_status_string(status), status))
+
+
+class SimResult(ctypes.Structure):
+    _fields_ = [("makespan", ctypes.c_double), ("base_makespan", ctypes.c_double),
+                ("total_work", ctypes.c_double), ("efficiency", ctypes.c_double),
+                ("max_deficit", ctypes.c_double), ("order_edges", ctypes.c_longlong),
+                ("violations", ctypes.c_longlong), ("deadlock", ctypes.c_int)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libdash_attn.so is not built (run "
+                           "`python -m scheduling_persistent_attn_amd.build`)")
+    L = ctypes.CDLL(LIB_PATH)
+    i, p, sz, d = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_double
+    L.dash_attn_tile_size.argtypes = [i, i]
+    L.dash_attn_tile_size.restype = i
+    L.dash_attn_bwd_workspace_size.argtypes = [i] * 7
+    L.dash_attn_bwd_workspace_size.restype = sz
+    L.dash_attn_fwd.argtypes = [p, p, p, p, p] + [i] * 6 + [p]
+    L.dash_attn_fwd.restype = i
+    L.dash_attn_bwd.argtypes = [p] * 9 + [i] * 7 + [p, sz, p]
+    L.dash_attn_bwd.restype = i
+    L.dash_attn_bwd_check.argtypes = [p, p]
+    L.dash_attn_bwd_check.restype = i
+    L.dash_status_string.argtypes = [i]
+    L.dash_status_string.restype = ctypes.c_char_p
+    L.dash_attn_bwd_grid_size.argtypes = [i, i, i]
+    L.dash_attn_bwd_grid_size.restype = i
+    L.dash_schedule_num_items.argtypes = [i, i, i]
+    L.dash_schedule_num_items.restype = i
+    L.dash_schedule_item_len.argtypes = [i] * 5
+    L.dash_schedule_item_len.restype = i
+    L.dash_schedule_task.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 4
+    L.dash_schedule_task.restype = i
+    L.dash_sim_run.argtypes = [i] * 7 + [d, d, d, ctypes.POINTER(SimResult)]
+    L.dash_sim_run.restype = i
+    _lib = L
+    return L
+
+
+# --- plain wrappers (same names as the C ABI) -------------------------------
+
+def dash_status_string(status):
+    return lib().dash_status_string(int(status)).decode()
+
+
+def dash_attn_tile_size(S, D):
+    return lib().dash_attn_tile_size(S, D)
+
+
+def dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, mask, schedule):
+    return lib().dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, mask, schedule)
+
+
+def dash_attn_bwd_grid_size(S, D, mask):
+    return lib().dash_attn_bwd_grid_size(S, D, mask)
+
+
+def dash_schedule_num_items(mask, schedule, N):
+    return lib().dash_schedule_num_items(mask, schedule, N)
+
+
+def dash_schedule_item_len(mask, schedule, N, G, item):
+    return lib().dash_schedule_item_len(mask, schedule, N, G, item)
+
+
+def dash_schedule_task(mask, schedule, N, G, item, step):
+    g, i, j, r = (ctypes.c_int() for _ in range(4))
+    st = lib().dash_schedule_task(mask, schedule, N, G, item, step,
+                                  ctypes.byref(g), ctypes.byref(i), ctypes.byref(j),
+                                  ctypes.byref(r))
+    if st != 0:
+        raise ValueError("task out of range")
+    return g.value, i.value, j.value, r.value
+
+
+def dash_sim_run(mask, schedule, N, G=1, groups=1, P=256, dispatch=1,
+                 c_full=1.0, c_diag=None, r=0.0):
+    if c_diag is None:
+        c_diag = c_full
+    out = SimResult()
+    st = lib().dash_sim_run(mask, schedule, N, G, groups, P, dispatch,
+                            float(c_full), float(c_diag), float(r), ctypes.byref(out))
+    if st != DASH_OK:
+        raise DashError(st, "dash_sim_run")
+    return out.as_dict()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _dims(q, k):
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    return B, S, Hq, Hkv, D
+
+
+def _check_tensors(named, dtype):
+    for name, t in named:
+        if t is None:
+            continue
+        if t.dtype != dtype:
+            raise TypeError("%s must be %s" % (name, dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def dash_attn_fwd(q, k, v, o, lse, mask, stream=None):
+    """Forward into preallocated o [B,S,Hq,D] bf16 and lse [B,Hq,S] fp32."""
+    import torch
+    _check_tensors([("q", q), ("k", k), ("v", v), ("o", o)], torch.bfloat16)
+    _check_tensors([("lse", lse)], torch.float32)
+    B, S, Hq, Hkv, D = _dims(q, k)
+    st = lib().dash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             B, Hq, Hkv, S, D, int(mask), _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_fwd")
+
+
+def dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, workspace,
+                  stream=None):
+    """Backward into preallocated dq, dk, dv; workspace is a uint8 device tensor."""
+    import torch
+    _check_tensors([("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)], torch.bfloat16)
+    _check_tensors([("lse", lse)], torch.float32)
+    B, S, Hq, Hkv, D = _dims(q, k)
+    st = lib().dash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                             _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(mask),
+                             int(schedule), _ptr(workspace),
+                             workspace.numel() if workspace is not None else 0,
+                             _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd")
+
+
+def dash_attn_bwd_check(workspace, stream=None):
+    st = lib().dash_attn_bwd_check(_ptr(workspace), _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd_check")
+
+
+# --- conveniences that allocate outputs with torch --------------------------
+
+def new_workspace(q, k, mask, schedule):
+    import torch
+    B, S, Hq, Hkv, D = _dims(q, k)
+    n = dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, int(mask), int(schedule))
+    if n == 0:
+        raise ValueError("invalid arguments for the backward workspace")
+    # torch's caching allocator returns 256-byte aligned blocks
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def forward(q, k, v, causal):
+    import torch
+    B, S, Hq, Hkv, D = _dims(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    dash_attn_fwd(q, k, v, o, lse, MASK_CAUSAL if causal else MASK_FULL)
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, causal, schedule=SHIFT, workspace=None, stream=None):
+    import torch
+    mask = MASK_CAUSAL if causal else MASK_FULL
+    if workspace is None:
+        workspace = new_workspace(q, k, mask, schedule)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, workspace, stream)
+    return dq, dk, dv

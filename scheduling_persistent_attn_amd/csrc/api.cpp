@@ -1,0 +1,298 @@
+// C ABI of libdash_attn.so: argument checks, workspace layout, launches.
+// See include/dash_attn.h for the contract of every entry point.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "../../include/dash_attn.h"
+#include "kernels.h"
+#include "schedule.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr double kWatchdogSeconds = 2.0;
+
+struct DeviceInfo {
+  bool ready = false;
+  int cus = 0;
+  long long wall_khz = 0;
+  int bpc[2][2][2] = {};  // [D==128][T==128][causal] resident blocks per CU
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_mu;
+
+int device_info(DeviceInfo** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DASH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.ready) {
+    int cus = 0, khz = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return DASH_ERR_HIP;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+      khz = 100000;
+    d.cus = cus;
+    d.wall_khz = khz;
+    const int cfgs[3][2] = {{64, 64}, {64, 128}, {128, 128}};
+    for (auto& cfg : cfgs)
+      for (int causal = 0; causal < 2; ++causal)
+        d.bpc[cfg[0] == 128][cfg[1] == 128][causal] =
+            dash::bwd_blocks_per_cu(cfg[0], cfg[1], causal != 0);
+    d.ready = true;
+  }
+  *out = &d;
+  return DASH_OK;
+}
+
+inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  int T = 0, N = 0, NW = 0;
+  size_t ctrl = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, total = 0;
+  long long n_counters = 0, n_rows = 0, n_dqacc = 0;
+};
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Pure argument checks (no device access).
+int check_shape(int B, int Hq, int Hkv, int S, int D, int mask, int schedule) {
+  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0) return DASH_ERR_SHAPE;
+  if (Hq % Hkv != 0) return DASH_ERR_SHAPE;
+  if (D != 64 && D != 128) return DASH_ERR_UNSUPPORTED;
+  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return DASH_ERR_SCHEDULE_MASK;
+  if (schedule < DASH_SCHED_NAIVE || schedule > DASH_SCHED_ATOMIC) return DASH_ERR_SCHEDULE_MASK;
+  return DASH_OK;
+}
+
+int make_layout(int B, int Hq, int S, int D, Layout* L) {
+  L->T = dash_attn_tile_size(S, D);
+  if (L->T == 0) return DASH_ERR_UNSUPPORTED;
+  L->N = (S + L->T - 1) / L->T;
+  L->NW = L->T / 32;
+  const long long rows = (long long)B * Hq * L->N * L->T;
+  L->n_rows = rows;
+  L->n_counters = (long long)B * Hq * L->N * L->NW;
+  L->n_dqacc = rows * D;
+  // every element offset the kernels form must fit in 32 bits
+  const long long elems = (long long)B * S * Hq * D;
+  if (elems >= (1LL << 31) || L->n_dqacc >= (1LL << 31)) return DASH_ERR_UNSUPPORTED;
+  size_t off = 0;
+  L->ctrl = off;
+  off += round256(64 * sizeof(int));
+  L->counters = off;
+  off += round256((size_t)L->n_counters * sizeof(int));
+  L->delta = off;
+  off += round256((size_t)rows * sizeof(float));
+  L->lse2 = off;
+  off += round256((size_t)rows * sizeof(float));
+  L->dqacc = off;
+  off += round256((size_t)L->n_dqacc * sizeof(float));
+  L->total = off;
+  return DASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dash_attn_tile_size(int S, int D) {
+  if (D == 64) return S <= 512 ? 64 : 128;
+  if (D == 128) return 128;
+  return 0;
+}
+
+size_t dash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int S, int D, int mask,
+                                    int schedule) {
+  if (check_shape(B, Hq, Hkv, S, D, mask, schedule) != DASH_OK) return 0;
+  Layout L;
+  if (make_layout(B, Hq, S, D, &L) != DASH_OK) return 0;
+  return L.total;
+}
+
+const char* dash_status_string(int status) {
+  switch (status) {
+    case DASH_OK: return "ok";
+    case DASH_ERR_NULL: return "a required pointer is NULL";
+    case DASH_ERR_SHAPE: return "invalid shape or misaligned pointer";
+    case DASH_ERR_UNSUPPORTED: return "unsupported head dim, size or schedule residency";
+    case DASH_ERR_SCHEDULE_MASK: return "invalid mask/schedule combination";
+    case DASH_ERR_WORKSPACE: return "workspace missing or too small";
+    case DASH_ERR_HIP: return "HIP runtime error";
+    case DASH_ERR_TIMEOUT: return "device watchdog fired in an ordered reduction";
+    default: return "unknown status";
+  }
+}
+
+int dash_attn_bwd_grid_size(int S, int D, int mask) {
+  const int T = dash_attn_tile_size(S, D);
+  if (T == 0 || (mask != 0 && mask != 1)) return 0;
+  DeviceInfo* d = nullptr;
+  if (device_info(&d) != DASH_OK) return 0;
+  return d->cus * d->bpc[D == 128][T == 128][mask];
+}
+
+int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int Hq, int Hkv, int S, int D, int mask, void* stream) {
+  int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_NAIVE);
+  if (st != DASH_OK) return st;
+  if (B == 0 || S == 0) return DASH_OK;
+  if (!q || !k || !v || !o || !lse) return DASH_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return DASH_ERR_SHAPE;
+  dash::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.S = S;
+  p.G = Hq / Hkv;
+  p.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+  if (dash::launch_fwd(D, mask == DASH_MASK_CAUSAL, p, (hipStream_t)stream) != hipSuccess)
+    return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
+                  int D, int mask, int schedule, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  int st = check_shape(B, Hq, Hkv, S, D, mask, schedule);
+  if (st != DASH_OK) return st;
+  Layout L;
+  st = make_layout(B, Hq, S, D, &L);
+  if (st != DASH_OK) return st;
+  if (schedule == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || (L.N % 2) != 0))
+    return DASH_ERR_SCHEDULE_MASK;
+  if (B == 0 || S == 0) return DASH_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return DASH_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return DASH_ERR_SHAPE;
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+    return DASH_ERR_WORKSPACE;
+
+  DeviceInfo* dev = nullptr;
+  st = device_info(&dev);
+  if (st != DASH_OK) return st;
+  const int bpc = dev->bpc[D == 128][L.T == 128][mask];
+  const int grid = dev->cus * bpc;
+  if (grid <= 0) return DASH_ERR_HIP;
+  const int G = Hq / Hkv;
+  const int ipg = dash::items_per_group(schedule, L.N);
+  // The shift family waits on chains that come later in the dispatch order,
+  // so a whole group of items must be able to run at once.
+  if ((schedule == DASH_SCHED_SHIFT || schedule == DASH_SCHED_SYMMETRIC_SHIFT) && ipg > grid)
+    return DASH_ERR_UNSUPPORTED;
+
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+
+  dash::PreParams pp;
+  pp.o = o;
+  pp.dout = dout;
+  pp.lse = lse;
+  pp.delta = (float*)(ws + L.delta);
+  pp.lse2 = (float*)(ws + L.lse2);
+  pp.counters = (int*)(ws + L.counters);
+  pp.ctrl = (int*)(ws + L.ctrl);
+  pp.dqacc = (float*)(ws + L.dqacc);
+  pp.n_counters = L.n_counters;
+  pp.n_dqacc = L.n_dqacc;
+  pp.zero_dqacc = schedule == DASH_SCHED_ATOMIC;
+  pp.B = B;
+  pp.Hq = Hq;
+  pp.S = S;
+  pp.D = D;
+  pp.NT = L.N * L.T;
+  if (dash::launch_preprocess(pp, s) != hipSuccess) return DASH_ERR_HIP;
+
+  dash::BwdParams bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.dout = dout;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.delta = pp.delta;
+  bp.lse2 = pp.lse2;
+  bp.dqacc = pp.dqacc;
+  bp.counters = pp.counters;
+  bp.ctrl = pp.ctrl;
+  bp.B = B;
+  bp.Hq = Hq;
+  bp.Hkv = Hkv;
+  bp.S = S;
+  bp.N = L.N;
+  bp.G = G;
+  bp.mask = mask;
+  bp.schedule = schedule;
+  bp.items_per_group = ipg;
+  bp.total_items = B * Hkv * ipg;
+  bp.scale = (float)(1.0 / __builtin_sqrt((double)D));
+  bp.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+  bp.spin_ticks = (long long)(kWatchdogSeconds * 1000.0 * (double)dev->wall_khz);
+  const int launch_grid = grid < bp.total_items ? grid : bp.total_items;
+  if (dash::launch_bwd_main(D, L.T, mask == DASH_MASK_CAUSAL, bp, launch_grid, s) != hipSuccess)
+    return DASH_ERR_HIP;
+
+  if (schedule == DASH_SCHED_ATOMIC) {
+    dash::FinParams fp;
+    fp.dqacc = pp.dqacc;
+    fp.dq = dq;
+    fp.B = B;
+    fp.Hq = Hq;
+    fp.S = S;
+    fp.N = L.N;
+    fp.scale = bp.scale;
+    if (dash::launch_finalize_atomic(D, L.T, fp, s) != hipSuccess) return DASH_ERR_HIP;
+  }
+  return DASH_OK;
+}
+
+int dash_attn_bwd_check(const void* workspace, void* stream) {
+  if (!workspace) return DASH_ERR_NULL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
+  int flag[2] = {0, 0};
+  if (hipMemcpy(flag, (const int*)workspace + 1, sizeof(flag), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return DASH_ERR_HIP;
+  return flag[0] ? DASH_ERR_TIMEOUT : DASH_OK;
+}
+
+int dash_schedule_num_items(int mask, int schedule, int N) {
+  if (N < 1 || (mask != 0 && mask != 1) || schedule < 0 || schedule > 4) return -1;
+  if (schedule == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || N % 2)) return -1;
+  return dash::items_per_group(schedule, N);
+}
+
+int dash_schedule_item_len(int mask, int schedule, int N, int G, int item) {
+  const int n = dash_schedule_num_items(mask, schedule, N);
+  if (n < 0 || G < 1 || item < 0 || item >= n) return -1;
+  return dash::item_len(mask, schedule, N, G, item);
+}
+
+int dash_schedule_task(int mask, int schedule, int N, int G, int item, int step, int* g, int* i,
+                       int* j, int* rank) {
+  const int len = dash_schedule_item_len(mask, schedule, N, G, item);
+  if (len < 0 || step < 0 || step >= len || !g || !i || !j || !rank) return -1;
+  const dash::Task t = dash::task_at(mask, schedule, N, G, item, step);
+  *g = t.g;
+  *i = t.i;
+  *j = t.j;
+  *rank = t.rank;
+  return 0;
+}
+
+}  // extern "C"

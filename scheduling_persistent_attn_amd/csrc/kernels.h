@@ -1,0 +1,72 @@
+// Kernel parameter blocks and launch entry points shared by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace dash {
+
+struct PreParams {
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;      // [B*Hq][NT]
+  float* lse2;       // [B*Hq][NT]
+  int* counters;     // n_counters ints, zeroed
+  int* ctrl;         // 64 ints, zeroed
+  float* dqacc;      // zeroed when zero_dqacc (atomic schedule)
+  long long n_counters;
+  long long n_dqacc;
+  int zero_dqacc;
+  int B, Hq, S, D, NT;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* delta;
+  const float* lse2;
+  float* dqacc;
+  int* counters;
+  int* ctrl;
+  int B, Hq, Hkv, S, N, G;
+  int mask, schedule;
+  int total_items, items_per_group;
+  float scale, scale_log2e;
+  long long spin_ticks;
+};
+
+struct FinParams {
+  const float* dqacc;
+  void* dq;
+  int B, Hq, S, N;
+  float scale;
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, S, G;
+  float scale_log2e;
+};
+
+// Persistent workgroups per compute unit for the backward kernel of (D, T,
+// causal); 0 if not instantiated.
+int bwd_blocks_per_cu(int D, int T, bool causal);
+int bwd_block_threads(int T);
+
+hipError_t launch_preprocess(const PreParams& p, hipStream_t s);
+hipError_t launch_bwd_main(int D, int T, bool causal, const BwdParams& p, int grid,
+                           hipStream_t s);
+hipError_t launch_finalize_atomic(int D, int T, const FinParams& p, hipStream_t s);
+hipError_t launch_fwd(int D, bool causal, const FwdParams& p, hipStream_t s);
+
+}  // namespace dash

@@ -1,0 +1,122 @@
+// Closed-form tile schedules, evaluated identically on the host and in the
+// kernels.
+//
+// A group is one (batch, key/value head); it has N key/value tiles i, N query
+// tiles j and G query heads g.  Task (g, i, j) is the work of KV tile i on Q
+// tile j of query head g; a causal mask keeps j >= i only.  One *item* is what
+// a persistent workgroup takes at a time: the chain of one KV tile over all G
+// heads, or for the symmetric shift the pair of KV tiles p and N-1-p.  Keeping
+// a KV tile's tasks contiguous on one unit keeps its dK/dV in registers
+// (DASH technical summary, section 2.1, constraints).
+//
+// rank(g, i, j) is the position of KV tile i in the fixed reduction order of
+// dQ tile (g, j):
+//   NAIVE / DESCENDING_Q : i, ascending KV order (section 1's rigid order;
+//                          section 2.2 A only reverses the walk over Q tiles)
+//   SHIFT, full          : (j - i) mod N -- chain i reaches Q tile j at step
+//                          (j - i) mod N of the cyclic walk i, i+1, ..., i-1
+//                          (section 2.2 B), so in lockstep every dQ tile is met
+//                          by exactly one chain per step, in this order
+//   SHIFT, causal        : j - i (the same walk without the masked tiles)
+//   SYMMETRIC_SHIFT      : phase 1 (dense block KV < N/2, Q >= N/2, cyclic):
+//                          (j - N/2 - i) mod N/2; phase 2 (the folded
+//                          triangles): j - i for Q < N/2, i for KV >= N/2
+//                          (section 2.2 B, symmetric shift; the fold geometry
+//                          is this library's reading of the two phases).
+// Item task lists for G > 1: the single-head list repeated per head (chains);
+// for the symmetric pair, phase 1 for every head, then the KV-p part of phase
+// 2 for every head, then the KV-(N-1-p) part for every head, which keeps the
+// lockstep free of conflicts with the same ranks as one head.
+#pragma once
+
+#ifdef __HIPCC__
+#define DASH_HD __host__ __device__ inline __attribute__((always_inline))
+#else
+#define DASH_HD inline
+#endif
+
+namespace dash {
+
+enum { MASK_FULL = 0, MASK_CAUSAL = 1 };
+enum { SCHED_NAIVE = 0, SCHED_DESC = 1, SCHED_SHIFT = 2, SCHED_SYM = 3, SCHED_ATOMIC = 4 };
+
+struct Task {
+  int g, i, j, rank;
+  int seg_begin;  // first task of a KV tile's run inside the item
+  int seg_end;    // last task of that run
+};
+
+DASH_HD int items_per_group(int schedule, int N) {
+  return schedule == SCHED_SYM ? N / 2 : N;
+}
+
+// Tasks of one KV chain per query head.
+DASH_HD int chain_len(int mask, int N, int i) { return mask == MASK_CAUSAL ? N - i : N; }
+
+DASH_HD int item_len(int mask, int schedule, int N, int G, int item) {
+  if (schedule == SCHED_SYM) return G * (N + 1);
+  return G * chain_len(mask, N, item);
+}
+
+// Number of key/value tiles reducing into any dQ tile j.
+DASH_HD int contributors(int mask, int N, int j) { return mask == MASK_CAUSAL ? j + 1 : N; }
+
+DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
+  Task t;
+  if (schedule == SCHED_SYM) {
+    const int h = N / 2, p = item;
+    const int len_a = G * (N - p);  // phase 1 + KV-p part of phase 2
+    if (step < len_a) {
+      t.i = p;
+      t.seg_begin = step == 0;
+      t.seg_end = step == len_a - 1;
+      if (step < G * h) {
+        t.g = step / h;
+        const int s = step - t.g * h;
+        t.j = h + (p + s) % h;
+        t.rank = s;
+      } else {
+        const int k = step - G * h, l1 = h - p;
+        t.g = k / l1;
+        const int s = k - t.g * l1;
+        t.j = p + s;
+        t.rank = s;
+      }
+    } else {
+      const int k = step - len_a, l2 = p + 1;
+      t.i = N - 1 - p;
+      t.seg_begin = k == 0;
+      t.seg_end = k == G * l2 - 1;
+      t.g = k / l2;
+      const int s = k - t.g * l2;
+      t.j = N - 1 - s;
+      t.rank = t.i;
+    }
+    return t;
+  }
+  const int i = item;
+  const int L = chain_len(mask, N, i);
+  t.i = i;
+  t.g = step / L;
+  const int s = step - t.g * L;
+  t.seg_begin = step == 0;
+  t.seg_end = step == G * L - 1;
+  const int first = mask == MASK_CAUSAL ? i : 0;
+  switch (schedule) {
+    case SCHED_DESC:
+      t.j = N - 1 - s;
+      t.rank = i;
+      break;
+    case SCHED_SHIFT:
+      t.j = mask == MASK_CAUSAL ? i + s : (i + s) % N;
+      t.rank = s;
+      break;
+    default:  // NAIVE, ATOMIC
+      t.j = first + s;
+      t.rank = i;
+      break;
+  }
+  return t;
+}
+
+}  // namespace dash

@@ -1,0 +1,62 @@
+"""Helpers shared by the GPU tests (not collected: no test_ prefix)."""
+
+import numpy as np
+import torch
+
+import scheduling_persistent_attn_amd as dash
+from scheduling_persistent_attn_amd.inputs import as_float64, make_inputs
+
+# tolerance of the deterministic backward against the float64 oracle, bf16
+# inputs and outputs, fp32 accumulation
+REL_L2 = 1e-2
+MAX_ABS = 2e-2
+
+
+def rel_l2(a, b):
+    den = np.linalg.norm(b.ravel())
+    return np.linalg.norm((a - b).ravel()) / (den if den > 0 else 1.0)
+
+
+def errors(got, ref):
+    return rel_l2(got, ref), float(np.max(np.abs(got - ref))) if ref.size else 0.0
+
+
+def run_forward(x, causal):
+    o, lse = dash.forward(x["q"], x["k"], x["v"], causal)
+    return o, lse
+
+
+def run_backward(x, o, lse, causal, schedule, workspace=None, stream=None):
+    return dash.backward(x["q"], x["k"], x["v"], o, x["do"], lse, causal, schedule,
+                         workspace=workspace, stream=stream)
+
+
+def gpu_inputs(B, S, Hq, Hkv, D, seed=1000):
+    return make_inputs(B, S, Hq, Hkv, D, seed=seed, device="cuda")
+
+
+def host64(t):
+    return as_float64(t)
+
+
+def contributors(causal, N, j):
+    return j + 1 if causal else N
+
+
+def expected_counters(B, Hq, S, D, causal):
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    NW = T // 32
+    want = np.zeros((B, Hq, N, NW), dtype=np.int64)
+    for j in range(N):
+        want[:, :, j, :] = contributors(causal, N, j)
+    return want
+
+
+def read_counters(workspace, B, Hq, S, D):
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    NW = T // 32
+    n = B * Hq * N * NW
+    ws = workspace.view(torch.int32)
+    return ws[64:64 + n].cpu().numpy().reshape(B, Hq, N, NW)

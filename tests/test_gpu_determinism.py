@@ -1,0 +1,89 @@
+"""Run-to-run bit identity of every deterministic schedule on the GPU.
+
+20 runs per schedule rotate over three streams with a seeded, varying amount
+of unrelated GPU work queued before each call, so that workgroups reach the
+ordered reductions in different orders; dq/dk/dv must not change by a bit.
+The atomic reference is run the same way and its spread is reported (it is
+the positive control that shows the harness can see non-determinism).
+"""
+
+import random
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import scheduling_persistent_attn_amd as dash
+
+sys.path.insert(0, __file__.rsplit("/", 1)[0])
+import gpu_util as gu  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+RUNS = 20
+
+CASES = [
+    # B, S, Hq, Hkv, D, causal
+    (1, 1024, 8, 2, 128, True),
+    (2, 1024, 4, 4, 64, False),
+    (1, 2048, 8, 8, 128, False),
+]
+
+
+def _perturb(rng, stream, scratch):
+    # unrelated work of random length ahead of the call on the same stream
+    with torch.cuda.stream(stream):
+        for _ in range(rng.randint(0, 6)):
+            scratch.mul_(1.0001)
+
+
+def _runs(case, sched):
+    B, S, Hq, Hkv, D, causal = case
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=2000)
+    o, lse = gu.run_forward(x, causal)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    rng = random.Random(1234 + sched)
+    scratch = torch.ones(1 << 22, device="cuda")
+    outs = []
+    for n in range(RUNS):
+        s = streams[n % 3]
+        _perturb(rng, s, scratch)
+        ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
+        with torch.cuda.stream(s):
+            dq, dk, dv = gu.run_backward(x, o, lse, causal, sched, workspace=ws, stream=s)
+        dash.dash_attn_bwd_check(ws, stream=s)
+        outs.append(tuple(t.view(torch.int16).cpu().numpy().copy() for t in (dq, dk, dv)))
+        if sched != dash.ATOMIC:
+            cnt = gu.read_counters(ws, B, Hq, S, D)
+            assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
+    return outs
+
+
+def _sched_list(case):
+    B, S, Hq, Hkv, D, causal = case
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    out = [dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT]
+    if causal and N % 2 == 0:
+        out.append(dash.SYMMETRIC_SHIFT)
+    return out
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_bit_identical_over_runs(case):
+    for sched in _sched_list(case):
+        print("determinism", case, "schedule", sched, flush=True)
+        outs = _runs(case, sched)
+        for n in range(1, RUNS):
+            for a, b in zip(outs[0], outs[n]):
+                assert np.array_equal(a, b), (sched, n)
+
+
+def test_atomic_reference_spread():
+    case = CASES[2]
+    outs = _runs(case, dash.ATOMIC)
+    differing = sum(1 for n in range(1, RUNS)
+                    if not np.array_equal(outs[0][0], outs[n][0]))
+    print("atomic reference: %d of %d runs differ from the first in dq" % (differing, RUNS - 1))
