@@ -126,6 +126,20 @@ __global__ __launch_bounds__(256) void bwd_preprocess(PreParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// The ordered hand-off of a dQ slice between workgroups.
+//
+// Every access to the fp32 dQ accumulator is a device-scope (sc1) buffer
+// load or store, i.e. it is performed at the device's coherence point and
+// never served from a stale line of this XCD's L2.  The hand-off therefore
+// needs no cache-wide writeback or invalidate:
+//   release: wait until this wave's sc1 stores are acknowledged (s_waitcnt),
+//            then store rank + 1 into the turn counter (sc1);
+//   acquire: poll the counter (sc1 loads) until it equals the rank; the
+//            accumulator loads are issued only after the poll loop exits.
+constexpr int kSC1 = 16;  // cache-policy operand of the buffer intrinsics: sc1
+
+__device__ __forceinline__ void order_point() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
 // Turn wait with a watchdog.  Executed by a whole wave; lane 0 polls.  Returns
 // false (and raises the workspace error flag) on timeout or if another wave
 // already raised it.
@@ -151,7 +165,7 @@ __device__ __forceinline__ bool wait_turn(const int* cnt, int rank, int* ctrl,
     }
   }
   ok = __shfl(ok, 0);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  order_point();
   return ok != 0;
 }
 
@@ -481,14 +495,16 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         const int rank = t.rank;
         const bool last = rank == contributors(mask, N, j) - 1;
         if (rank > 0) wait_turn(cnt, rank, p.ctrl, p.spin_ticks, lane);
+        const __amdgpu_buffer_rsrc_t racc =
+            __builtin_amdgcn_make_buffer_rsrc(acc, 0, C::MQ * 4096, 0x00020000);
         // one 32-row block at a time keeps the live set small
 #pragma unroll
         for (int m = 0; m < C::MQ; ++m) {
-          float* const am = acc + (m * 4 * 64 + lane) * 4;
+          const int am = (m * 4 * 64 + lane) * 16;  // byte offset in the slice
           if (rank > 0) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-              const f32x4 old = *reinterpret_cast<const f32x4*>(am + q4 * 256);
+              const f32x4 old = __builtin_amdgcn_raw_buffer_load_b128(racc, am + q4 * 1024, 0, kSC1);
 #pragma unroll
               for (int e = 0; e < 4; ++e) dq[m][4 * q4 + e] = old[e] + dq[m][4 * q4 + e];
             }
@@ -497,7 +513,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
               const f32x4 x = {dq[m][4 * q4], dq[m][4 * q4 + 1], dq[m][4 * q4 + 2], dq[m][4 * q4 + 3]};
-              *reinterpret_cast<f32x4*>(am + q4 * 256) = x;
+              __builtin_amdgcn_raw_buffer_store_b128(x, racc, am + q4 * 1024, 0, kSC1);
             }
           } else {
             // final value: dQ = scale * sum, bf16
@@ -514,7 +530,10 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // release: all of this wave's accumulator stores acknowledged first
+        order_point();
+        __builtin_amdgcn_s_waitcnt(0);
+        order_point();
         if (lane == 0)
           __hip_atomic_store(cnt, rank + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }

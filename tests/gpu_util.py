@@ -6,10 +6,15 @@ import torch
 import scheduling_persistent_attn_amd as dash
 from scheduling_persistent_attn_amd.inputs import as_float64, make_inputs
 
-# tolerance of the deterministic backward against the float64 oracle, bf16
-# inputs and outputs, fp32 accumulation
+# Tolerance of the backward against the float64 oracle (bf16 inputs, fp32
+# accumulation, bf16 outputs): rel-L2 <= 1e-2 and an absolute error of at most
+# 2e-2 beyond the rounding of the output to bf16 itself.  Round-to-nearest to
+# bf16 (8 significant bits) moves a value x by at most 2^-8 |x|, which alone
+# exceeds 2e-2 once |x| > 5.12, so the absolute bar is applied to
+# |got - ref| - 2^-8 |ref|.
 REL_L2 = 1e-2
 MAX_ABS = 2e-2
+BF16_HALF_ULP_REL = 2.0 ** -8
 
 
 def rel_l2(a, b):
@@ -18,7 +23,16 @@ def rel_l2(a, b):
 
 
 def errors(got, ref):
-    return rel_l2(got, ref), float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    """(rel-L2, max-abs beyond bf16 output rounding, plain max-abs)."""
+    if not ref.size:
+        return 0.0, 0.0, 0.0
+    d = np.abs(got - ref)
+    return (rel_l2(got, ref), float(np.max(d - BF16_HALF_ULP_REL * np.abs(ref))),
+            float(np.max(d)))
+
+
+def within(e):
+    return e[0] <= REL_L2 and e[1] <= MAX_ABS
 
 
 def run_forward(x, causal):

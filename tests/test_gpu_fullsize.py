@@ -1,0 +1,72 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+For each large configuration every applicable schedule runs on the whole
+problem; the float64 oracle is evaluated for one sampled (batch, kv head)
+group -- all of its query heads, so dK/dV of that kv head are complete -- and
+compared element by element.  The rest of the output is checked through
+properties that hold at any size: finite values and, for the deterministic
+schedules, every turn counter ending at its contributor count.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import scheduling_persistent_attn_amd as dash
+from oracle import attention as oa
+
+sys.path.insert(0, __file__.rsplit("/", 1)[0])
+import gpu_util as gu  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = {
+    # name: (B, S, Hq, Hkv, D, causal, sampled (batch, kv head))
+    "llama8b_causal": (4, 4096, 32, 8, 128, True, (3, 5)),
+    "dit_full": (2, 4096, 24, 24, 64, False, (1, 17)),
+    "long_full": (1, 16384, 32, 32, 128, False, (0, 31)),
+    "qwen7b_causal": (1, 16384, 28, 4, 128, True, (0, 3)),
+}
+
+
+def _schedules(causal, N):
+    out = [dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT, dash.ATOMIC]
+    if causal and N % 2 == 0:
+        out.append(dash.SYMMETRIC_SHIFT)
+    return out
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_fullsize_sampled_parity(name):
+    B, S, Hq, Hkv, D, causal, (sb, skv) = CONFIGS[name]
+    G = Hq // Hkv
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    print("fullsize", name, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D)
+    o, lse = gu.run_forward(x, causal)
+    torch.cuda.synchronize()
+    hs = list(range(skv * G, (skv + 1) * G))
+    h = {k: gu.host64(v[sb:sb + 1]) for k, v in x.items()}
+    ref = oa.attention_backward_sampled(h["q"], h["k"], h["v"], h["do"], causal, [skv])[skv]
+    rdq, rdk, rdv = ref
+    for sched in _schedules(causal, N):
+        print("  schedule", sched, flush=True)
+        ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
+        dq, dk, dv = gu.run_backward(x, o, lse, causal, sched, workspace=ws)
+        dash.dash_attn_bwd_check(ws)
+        for t in (dq, dk, dv):
+            assert torch.isfinite(t.float()).all()
+        got = (gu.host64(dq[sb:sb + 1, :, hs]), gu.host64(dk[sb:sb + 1, :, skv]),
+               gu.host64(dv[sb:sb + 1, :, skv]))
+        for nm, g, r in zip(("dq", "dk", "dv"), got, (rdq, rdk, rdv)):
+            e = gu.errors(g, r)
+            print("    %s rel-l2 %.3e max-abs(excess) %.3e max-abs %.3e (ref max %.3e)"
+                  % ((nm,) + e + (np.max(np.abs(r)),)))
+            assert gu.within(e), (nm, sched, e)
+        if sched != dash.ATOMIC:
+            cnt = gu.read_counters(ws, B, Hq, S, D)
+            assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
+        del ws, dq, dk, dv
