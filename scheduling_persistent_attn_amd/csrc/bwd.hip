@@ -485,11 +485,13 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
       const int tile = (b * p.Hq + h) * N + j;
       float* const acc = p.dqacc + (tile * C::NW + w) * (C::MQ * 1024);
       if constexpr (atomic_dq) {
+        // element r of row block m of lane l at (m*16 + r)*64 + l: each
+        // atomic instruction covers 64 consecutive floats
 #pragma unroll
         for (int m = 0; m < C::MQ; ++m)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            unsafeAtomicAdd(acc + ((m * 4 + (r >> 2)) * 64 + lane) * 4 + (r & 3), dq[m][r]);
+            unsafeAtomicAdd(acc + (m * 16 + r) * 64 + lane, dq[m][r]);
       } else {
         int* const cnt = p.counters + tile * C::NW + w;
         const int rank = t.rank;
@@ -567,17 +569,18 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Atomic reference only: dQ partial sums (kernel lane order) -> bf16 dq.
+// Atomic reference only: dQ partial sums -> bf16 dq.  One thread per float of
+// the accumulator, laid out as [tile][wave slice][row block m][r][lane].
 template <int D, int T>
 __global__ __launch_bounds__(256) void bwd_finalize(FinParams p) {
   constexpr int NW = T / 32, DB = D / 32, MQ = DB;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)p.B * p.Hq * p.N * NW * MQ * 4 * 64;
+  const long long total = (long long)p.B * p.Hq * p.N * NW * MQ * 16 * 64;
   if (idx >= total) return;
   const int lane = (int)(idx % 64);
   long long rest = idx / 64;
-  const int q4 = (int)(rest % 4);
-  rest /= 4;
+  const int r = (int)(rest % 16);
+  rest /= 16;
   const int m = (int)(rest % MQ);
   rest /= MQ;
   const int w = (int)(rest % NW);
@@ -586,16 +589,11 @@ __global__ __launch_bounds__(256) void bwd_finalize(FinParams p) {
   const long long bh = rest / p.N;
   const int b = (int)(bh / p.Hq), h = (int)(bh % p.Hq);
   const int qg = w / DB, db = w % DB;
-  const f32x4 x = reinterpret_cast<const f32x4*>(p.dqacc)[idx];
-  bf16* const gdq = (bf16*)p.dq;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int ql = 32 * (qg * MQ + m) + 8 * q4 + 4 * (lane >> 5) + e;
-    const int row = j * T + ql;
-    if (row < p.S)
-      gdq[((size_t)((size_t)b * p.S + row) * p.Hq + h) * D + 32 * db + (lane & 31)] =
-          (bf16)(x[e] * p.scale);
-  }
+  const int ql = 32 * (qg * MQ + m) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  const int row = j * T + ql;
+  if (row < p.S)
+    ((bf16*)p.dq)[((size_t)((size_t)b * p.S + row) * p.Hq + h) * D + 32 * db + (lane & 31)] =
+        (bf16)(p.dqacc[idx] * p.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -666,7 +664,7 @@ hipError_t launch_bwd_main(int D, int T, bool causal, const BwdParams& p, int gr
 }
 
 hipError_t launch_finalize_atomic(int D, int T, const FinParams& p, hipStream_t s) {
-  const long long total = (long long)p.B * p.Hq * p.N * (T / 32) * (D / 32) * 4 * 64;
+  const long long total = (long long)p.B * p.Hq * p.N * (T / 32) * (D / 32) * 16 * 64;
   const long long blocks = (total + 255) / 256;
   if (blocks < 1) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
