@@ -129,6 +129,9 @@ def main():
     ap.add_argument("--schedules", default="naive,descending_q,shift,symmetric_shift,atomic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -138,6 +141,16 @@ def main():
     import torch
     import scheduling_persistent_attn_amd as dash
     from scheduling_persistent_attn_amd.inputs import make_inputs
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
 
     cfg = CONFIGS[args.config]
     B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]

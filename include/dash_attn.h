@@ -95,9 +95,10 @@ int dash_attn_tile_size(int S, int D);
  *   ctrl      64 x int32   [0] work-dispatch counter, [1] watchdog flag,
  *                          [2] number of waits that timed out
  *   counters  B*Hq*N*W int32: the turn counter of every (batch, query head,
- *             dQ tile, wave slice); after a deterministic backward each holds
- *             the number of key/value tiles that reduced into that dQ tile
- *             (N = ceil(S/T), W = T/32)
+ *             dQ tile, slice) -- a slice is one 32-feature or 32-row part of
+ *             one 64-row pass over the tile; after a deterministic backward
+ *             each holds the number of key/value tiles that reduced into that
+ *             dQ tile (N = ceil(S/T), W = T*T/2048)
  *   delta     B*Hq*N*T fp32: rowsum(dO * O), zero past S
  *   lse2      B*Hq*N*T fp32: lse * log2(e), +inf past S
  *   dqacc     B*Hq*N*T*D fp32: dQ partial sums in the kernels' lane order

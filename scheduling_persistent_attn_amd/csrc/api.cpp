@@ -73,7 +73,8 @@ int make_layout(int B, int Hq, int S, int D, Layout* L) {
   L->T = dash_attn_tile_size(S, D);
   if (L->T == 0) return DASH_ERR_UNSUPPORTED;
   L->N = (S + L->T - 1) / L->T;
-  L->NW = L->T / 32;
+  // one turn counter per (dQ tile, 64-row pass, wave): T/64 * T/32 per tile
+  L->NW = (L->T / 64) * (L->T / 32);
   const long long rows = (long long)B * Hq * L->N * L->T;
   L->n_rows = rows;
   L->n_counters = (long long)B * Hq * L->N * L->NW;
