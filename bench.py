@@ -2,24 +2,34 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-One step = one dash_attn_bwd call (preprocess + persistent backward, plus the
-finalize pass for the atomic reference) over one batch of synthetic bf16 input
-already resident in HBM.  Each schedule is timed separately: W untimed calls,
-then K calls between two device synchronisations, with HIP events recorded on
-the call's stream around every call.  Prints one JSON line.
+One step = one whole backward (dash_attn_bwd_prepare then dash_attn_bwd_run,
+which together are exactly dash_attn_bwd: preprocess, persistent backward, and
+for the atomic reference the finalize pass) over one batch of synthetic bf16
+input already resident in HBM.  Each schedule is timed separately: W untimed
+steps, then K steps between two device synchronisations, with HIP events
+recorded on the call's stream before the preprocess, between the phases and
+after the persistent kernel.  Prints one JSON line.
 
-The headline value is the throughput of the fastest deterministic schedule in
-TFLOP/s with FLOPs = 10*B*Hq*S^2*D (halved for a causal mask).  The roofline
-object prices the persistent backward kernel against the bf16 dense MFMA peak.
-The cpu_baseline object times the float64 oracle on a bounded sample of the
-same workload on the host cores.
+The headline value is the whole-step throughput of the fastest deterministic
+schedule in TFLOP/s with FLOPs = 10*B*Hq*S^2*D (halved for a causal mask).  The
+roofline object prices the persistent backward kernel alone (events around
+dash_attn_bwd_run) against the bf16 dense MFMA peak; its traffic figure is the
+calibrated FETCH_SIZE + WRITE_SIZE of that kernel read from the committed
+rocprofv3 summary, reported only while that summary's kernel-source hash
+matches the current source.  The cpu_baseline object times the float64 oracle
+on a bounded sample of the same workload on the host cores.
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "scheduling_persistent_attn_amd", "csrc", "bwd.hip")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
@@ -59,30 +69,57 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
     dk = torch.empty_like(x["k"])
     dv = torch.empty_like(x["v"])
     stream = torch.cuda.current_stream()
+    Hkv = x["k"].shape[2]
 
-    def call():
-        dash.dash_attn_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, dq, dk, dv,
-                           mask, sched, ws, stream)
+    # events on the stream the kernels are launched on
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record(stream)
+        dash.dash_attn_bwd_prepare(o, x["do"], lse, tuple(x["q"].shape), Hkv, mask, sched,
+                                   ws, stream)
+        if e:
+            e[1].record(stream)
+        dash.dash_attn_bwd_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, mask, sched,
+                               ws, stream)
+        if e:
+            e[2].record(stream)
 
     for _ in range(warmup):
-        call()
+        step()
     dash.dash_attn_bwd_check(ws, stream)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for n in range(steps):
-        starts[n].record(stream)
-        call()
-        ends[n].record(stream)
+        step(ev[n])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dash.dash_attn_bwd_check(ws, stream)
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    mean_ms = sum(per) / len(per)
-    return {"ms_mean": mean_ms, "ms_median": per[len(per) // 2], "ms_p10": per[len(per) // 10],
+    per = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    kern = [e[1].elapsed_time(e[2]) for e in ev]
+    return {"ms_mean": sum(per) / len(per), "ms_median": per[len(per) // 2],
+            "ms_p10": per[len(per) // 10],
             "ms_p90": per[min(len(per) - 1, (9 * len(per)) // 10)],
+            "kernel_ms_mean": sum(kern) / len(kern),
             "wall_ms_per_step": 1e3 * wall / steps}
+
+
+def committed_traffic(config, schedule):
+    """Calibrated HBM bytes per launch of the persistent kernel, from the
+    committed rocprofv3 summary; None if there is none or it was taken on a
+    different kernel source."""
+    path = os.path.join(ROOT, "profiles", "bwd_main_%s.md" % config)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m:
+        return None
+    if hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest() != m.group(1):
+        return None
+    m = re.search(r"traffic_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" % re.escape(schedule), text)
+    return float(m.group(1)) if m else None
 
 
 def cpu_baseline(cfg, budget_s=20.0):
@@ -168,10 +205,11 @@ def main():
             continue
         r = time_schedule(dash, x, o, lse, cfg, sched, args.steps, args.warmup)
         r["tflops"] = fl / (r["ms_mean"] * 1e-3) / 1e12
+        r["kernel_tflops"] = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
         r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
         results[name] = r
-        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak" % (name, r["ms_mean"], r["tflops"],
-                                                               r["pct_peak"]))
+        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak  (kernel %.3f ms)"
+            % (name, r["ms_mean"], r["tflops"], r["pct_peak"], r["kernel_ms_mean"]))
     det = {k: v for k, v in results.items() if k != "atomic"}
     best = max(det, key=lambda k: det[k]["tflops"])
     atomic = results.get("atomic")
@@ -201,13 +239,15 @@ def main():
                           for kk, vv in v.items()} for k, v in results.items()},
         "roofline": {
             "bound": "mfma",
-            # algorithmic FLOPs of one call / mean event-timed duration of the
-            # call (preprocess + persistent kernel; the preprocess is ~1%)
-            "achieved": round(bestr["tflops"], 3),
+            # algorithmic FLOPs of one launch / mean event-timed duration of
+            # the persistent kernel (events around dash_attn_bwd_run)
+            "kernel": "bwd_main (%s)" % best,
+            "achieved": round(bestr["kernel_tflops"], 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(bestr["tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "frac": round(bestr["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+            # calibrated FETCH_SIZE + WRITE_SIZE bytes per launch
+            "traffic": committed_traffic(args.config, best),
         },
     }
     if not args.no_cpu_baseline:

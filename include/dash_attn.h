@@ -134,6 +134,30 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                   int schedule, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* The two phases of dash_attn_bwd, for callers that want to schedule or time
+ * them separately (same arguments and checks; pointers a phase does not read
+ * may be NULL).
+ *
+ * dash_attn_bwd_prepare: the per-row preprocessing of the technical summary's
+ * section 2.1 -- delta = rowsum(dout * o) and lse * log2(e) into the
+ * workspace -- and the reset of the work-dispatch counter, the watchdog flag
+ * and every turn counter (and, for ATOMIC, the dQ accumulator).
+ *
+ * dash_attn_bwd_run: the persistent backward over the schedule's items (and,
+ * for ATOMIC, the pass that converts the fp32 accumulator to bf16 dq).  It
+ * requires that dash_attn_bwd_prepare ran on this workspace, with the same
+ * shape, mask and schedule, after the previous run: the turn counters must
+ * start at zero, else the ordered reduction waits until the watchdog fires
+ * (DASH_ERR_TIMEOUT from dash_attn_bwd_check). */
+int dash_attn_bwd_prepare(const void* o, const void* dout, const float* lse, int B,
+                          int Hq, int Hkv, int S, int D, int mask, int schedule,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+int dash_attn_bwd_run(const void* q, const void* k, const void* v,
+                      const void* dout, void* dq, void* dk, void* dv, int B,
+                      int Hq, int Hkv, int S, int D, int mask, int schedule,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Waits for the stream, then reports DASH_ERR_TIMEOUT if the watchdog of the
  * last backward that used this workspace fired, DASH_ERR_HIP on a runtime
  * error, else DASH_OK.  Reads 8 bytes of the workspace. */

@@ -14,7 +14,7 @@ The pages give no weights and no definition of depth.  Reading used here:
 * consecutive tasks of an item: F(prev) -> S(next), weight 0;
 * consecutive items on one worker: F(last task) -> S(first task), weight 0;
 * the accumulation order of a dQ tile: F(rank q) -> R(rank q+1), weight 0 --
-  these are the "added zero-weight edges" of Lemma 1;
+  these are the zero-weight edges that Lemma 1 adds;
 * depth(x) = longest weighted path from any source to x (the earliest time
   at which x can happen); critical path = largest depth.
 

@@ -19,13 +19,13 @@ Schedules (DASH technical summary, section 2.2):
 * DESCENDING_Q -- the same chains walk their Q tiles from the last one down
   to the first (section 2.2 A); the reduction order is unchanged.
 * SHIFT -- full mask: the unit working on KV tile i visits Q tiles
-  i, i+1, ..., N-1, 0, ..., i-1 (section 2.2 B).  The pages' sentence says it
-  processes "KV blocks" in that cyclic order; since a KV tile's work must stay
-  on one unit (section 2.1) the cycle is read as running over the Q tiles of
-  chain i.  The reduction order of each dQ tile is the order in which the
-  chains reach it when all chains advance in lockstep ("naturally ordered
-  without conflicts").  With a causal mask the same cycle is used with the
-  masked tiles left out.
+  i, i+1, ..., N-1, 0, ..., i-1 (section 2.2 B).  The page words the cycle as
+  one over KV blocks; since a KV tile's work must stay on one unit (section
+  2.1) the cycle is read as running over the Q tiles of chain i.  The
+  reduction order of each dQ tile is the order in which the chains reach it
+  when all chains advance in lockstep, which the page describes as an order
+  that arises by itself with no two chains meeting one dQ tile at once.
+  With a causal mask the same cycle is used with the masked tiles left out.
 * SYMMETRIC_SHIFT -- causal mask, N even: one unit takes the KV tiles p and
   N-1-p (section 2.2 B, symmetric shift), which together have N+1 tasks.
   Phase 1 is the dense block {KV < N/2} x {Q >= N/2}, walked as a cyclic

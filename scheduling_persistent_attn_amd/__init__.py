@@ -29,7 +29,7 @@ DASH_ERR_TIMEOUT = 7
 
 SYMBOLS = (
     "dash_attn_tile_size", "dash_attn_bwd_workspace_size", "dash_attn_fwd",
-    "dash_attn_bwd", "dash_attn_bwd_check", "dash_status_string",
+    "dash_attn_bwd", "dash_attn_bwd_prepare", "dash_attn_bwd_run", "dash_attn_bwd_check", "dash_status_string",
     "dash_attn_bwd_grid_size", "dash_schedule_num_items",
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run",
 )
@@ -72,6 +72,10 @@ def lib():
     L.dash_attn_fwd.restype = i
     L.dash_attn_bwd.argtypes = [p] * 9 + [i] * 7 + [p, sz, p]
     L.dash_attn_bwd.restype = i
+    L.dash_attn_bwd_prepare.argtypes = [p] * 3 + [i] * 7 + [p, sz, p]
+    L.dash_attn_bwd_prepare.restype = i
+    L.dash_attn_bwd_run.argtypes = [p] * 7 + [i] * 7 + [p, sz, p]
+    L.dash_attn_bwd_run.restype = i
     L.dash_attn_bwd_check.argtypes = [p, p]
     L.dash_attn_bwd_check.restype = i
     L.dash_status_string.argtypes = [i]
@@ -192,6 +196,37 @@ def dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, workspace,
                              _stream(stream))
     if st != DASH_OK:
         raise DashError(st, "dash_attn_bwd")
+
+
+def dash_attn_bwd_prepare(o, dout, lse, q_shape, kv_heads, mask, schedule, workspace,
+                          stream=None):
+    """First phase of dash_attn_bwd (delta, lse*log2e, counter reset).
+    q_shape is (B, S, Hq, D); kv_heads is Hkv."""
+    import torch
+    _check_tensors([("o", o), ("dout", dout)], torch.bfloat16)
+    _check_tensors([("lse", lse)], torch.float32)
+    B, S, Hq, D = q_shape
+    st = lib().dash_attn_bwd_prepare(_ptr(o), _ptr(dout), _ptr(lse), B, Hq, int(kv_heads), S,
+                                     D, int(mask), int(schedule), _ptr(workspace),
+                                     workspace.numel() if workspace is not None else 0,
+                                     _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd_prepare")
+
+
+def dash_attn_bwd_run(q, k, v, dout, dq, dk, dv, mask, schedule, workspace, stream=None):
+    """Second phase of dash_attn_bwd (the persistent backward kernel)."""
+    import torch
+    _check_tensors([("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)], torch.bfloat16)
+    B, S, Hq, Hkv, D = _dims(q, k)
+    st = lib().dash_attn_bwd_run(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, Hq, Hkv, S, D, int(mask), int(schedule),
+                                 _ptr(workspace),
+                                 workspace.numel() if workspace is not None else 0,
+                                 _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd_run")
 
 
 def dash_attn_bwd_check(workspace, stream=None):

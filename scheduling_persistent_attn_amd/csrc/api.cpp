@@ -163,19 +163,41 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   return DASH_OK;
 }
 
-int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
-                  int D, int mask, int schedule, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Everything a backward launch needs, checked once.
+struct BwdPlan {
+  Layout L;
+  int grid = 0;
+  dash::PreParams pp;
+  dash::BwdParams bp;
+  dash::FinParams fp;
+};
+
+// Validates the arguments of a backward and fills the launch parameters.
+// Sets *empty for B == 0 or S == 0 (nothing to launch).  The pointers that a
+// phase does not use may be NULL: `need` selects which are required
+// (1 = preprocess inputs, 2 = main-kernel inputs and outputs).
+int plan_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
+             int D, int mask, int schedule, void* workspace, size_t workspace_bytes, int need,
+             BwdPlan* P, bool* empty) {
+  *empty = false;
   int st = check_shape(B, Hq, Hkv, S, D, mask, schedule);
   if (st != DASH_OK) return st;
-  Layout L;
+  Layout& L = P->L;
   st = make_layout(B, Hq, S, D, &L);
   if (st != DASH_OK) return st;
   if (schedule == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || (L.N % 2) != 0))
     return DASH_ERR_SCHEDULE_MASK;
-  if (B == 0 || S == 0) return DASH_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return DASH_ERR_NULL;
+  if (B == 0 || S == 0) {
+    *empty = true;
+    return DASH_OK;
+  }
+  if ((need & 1) && (!o || !dout || !lse)) return DASH_ERR_NULL;
+  if ((need & 2) && (!q || !k || !v || !dout || !dq || !dk || !dv)) return DASH_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4))
@@ -197,9 +219,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
     return DASH_ERR_UNSUPPORTED;
 
   char* ws = (char*)workspace;
-  hipStream_t s = (hipStream_t)stream;
-
-  dash::PreParams pp;
+  dash::PreParams& pp = P->pp;
   pp.o = o;
   pp.dout = dout;
   pp.lse = lse;
@@ -216,9 +236,8 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   pp.S = S;
   pp.D = D;
   pp.NT = L.N * L.T;
-  if (dash::launch_preprocess(pp, s) != hipSuccess) return DASH_ERR_HIP;
 
-  dash::BwdParams bp;
+  dash::BwdParams& bp = P->bp;
   bp.q = q;
   bp.k = k;
   bp.v = v;
@@ -244,22 +263,67 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   bp.scale = (float)(1.0 / __builtin_sqrt((double)D));
   bp.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   bp.spin_ticks = (long long)(kWatchdogSeconds * 1000.0 * (double)dev->wall_khz);
-  const int launch_grid = grid < bp.total_items ? grid : bp.total_items;
-  if (dash::launch_bwd_main(D, L.T, mask == DASH_MASK_CAUSAL, bp, launch_grid, s) != hipSuccess)
-    return DASH_ERR_HIP;
+  P->grid = grid < bp.total_items ? grid : bp.total_items;
 
-  if (schedule == DASH_SCHED_ATOMIC) {
-    dash::FinParams fp;
-    fp.dqacc = pp.dqacc;
-    fp.dq = dq;
-    fp.B = B;
-    fp.Hq = Hq;
-    fp.S = S;
-    fp.N = L.N;
-    fp.scale = bp.scale;
-    if (dash::launch_finalize_atomic(D, L.T, fp, s) != hipSuccess) return DASH_ERR_HIP;
-  }
+  dash::FinParams& fp = P->fp;
+  fp.dqacc = pp.dqacc;
+  fp.dq = dq;
+  fp.B = B;
+  fp.Hq = Hq;
+  fp.S = S;
+  fp.N = L.N;
+  fp.scale = bp.scale;
   return DASH_OK;
+}
+
+int launch_main_phase(const BwdPlan& P, int D, int mask, int schedule, hipStream_t s) {
+  if (dash::launch_bwd_main(D, P.L.T, mask == DASH_MASK_CAUSAL, P.bp, P.grid, s) != hipSuccess)
+    return DASH_ERR_HIP;
+  if (schedule == DASH_SCHED_ATOMIC &&
+      dash::launch_finalize_atomic(D, P.L.T, P.fp, s) != hipSuccess)
+    return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
+                  int D, int mask, int schedule, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  BwdPlan P;
+  bool empty = false;
+  int st = plan_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule,
+                    workspace, workspace_bytes, 3, &P, &empty);
+  if (st != DASH_OK || empty) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
+  return launch_main_phase(P, D, mask, schedule, s);
+}
+
+int dash_attn_bwd_prepare(const void* o, const void* dout, const float* lse, int B, int Hq,
+                          int Hkv, int S, int D, int mask, int schedule, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  BwdPlan P;
+  bool empty = false;
+  int st = plan_bwd(nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr, B, Hq,
+                    Hkv, S, D, mask, schedule, workspace, workspace_bytes, 1, &P, &empty);
+  if (st != DASH_OK || empty) return st;
+  if (dash::launch_preprocess(P.pp, (hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
+int dash_attn_bwd_run(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                      void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, int mask,
+                      int schedule, void* workspace, size_t workspace_bytes, void* stream) {
+  BwdPlan P;
+  bool empty = false;
+  int st = plan_bwd(q, k, v, nullptr, dout, nullptr, dq, dk, dv, B, Hq, Hkv, S, D, mask,
+                    schedule, workspace, workspace_bytes, 2, &P, &empty);
+  if (st != DASH_OK || empty) return st;
+  return launch_main_phase(P, D, mask, schedule, (hipStream_t)stream);
 }
 
 int dash_attn_bwd_check(const void* workspace, void* stream) {

@@ -6,7 +6,7 @@
 //
 // Events per task: S, E, R, F.  Weights: S->E = c (c_diag on a causal
 // diagonal tile), R->F = r, all other edges 0.  Order edges F(rank q) ->
-// R(rank q+1) per dQ tile are the "added zero-weight edges".  The replay
+// R(rank q+1) per dQ tile are the zero-weight edges that Lemma 1 adds.  The replay
 // advances workers in time order (and decides the dynamic dispatch); the DAG
 // pass computes longest paths in topological order, with and without the
 // order edges.

@@ -183,3 +183,32 @@ def test_simulator_rejects():
         dash.dash_sim_run(sch.FULL, sch.SYMMETRIC_SHIFT, 4)
     with pytest.raises(dash.DashError):
         dash.dash_sim_run(sch.FULL, sch.SHIFT, 0)
+
+
+def test_phase_validation_before_device():
+    p = ctypes.c_void_p
+    L = dash.lib()
+    a = p(1 << 12)
+    # prepare: o, dout, lse are required; q/k/v/dq/dk/dv are not read
+    assert L.dash_attn_bwd_prepare(None, a, a, 1, 2, 2, 256, 64, 0, 0, a, 1 << 30,
+                                   None) == dash.DASH_ERR_NULL
+    assert L.dash_attn_bwd_prepare(a, a, a, 1, 3, 2, 256, 64, 0, 0, a, 1 << 30,
+                                   None) == dash.DASH_ERR_SHAPE
+    assert L.dash_attn_bwd_prepare(a, a, a, 1, 2, 2, 256, 64, 0, 0, a, 16,
+                                   None) == dash.DASH_ERR_WORKSPACE
+    assert L.dash_attn_bwd_prepare(a, a, a, 1, 2, 2, 256, 64, 0, 3, a, 1 << 30,
+                                   None) == dash.DASH_ERR_SCHEDULE_MASK
+    assert L.dash_attn_bwd_prepare(None, None, None, 1, 2, 2, 0, 64, 0, 0, None, 0,
+                                   None) == dash.DASH_OK
+    # run: q, k, v, dout, dq, dk, dv are required; o and lse are not read
+    args = [a] * 7 + [1, 2, 2, 256, 64, 0, 0, a, 1 << 30, None]
+    for n in range(7):
+        bad = list(args)
+        bad[n] = None
+        assert L.dash_attn_bwd_run(*bad) == dash.DASH_ERR_NULL, n
+    bad = list(args)
+    bad[11] = 80
+    assert L.dash_attn_bwd_run(*bad) == dash.DASH_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[14] = None
+    assert L.dash_attn_bwd_run(*bad) == dash.DASH_ERR_WORKSPACE

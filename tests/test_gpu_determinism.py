@@ -87,3 +87,25 @@ def test_atomic_reference_spread():
     differing = sum(1 for n in range(1, RUNS)
                     if not np.array_equal(outs[0][0], outs[n][0]))
     print("atomic reference: %d of %d runs differ from the first in dq" % (differing, RUNS - 1))
+
+
+@pytest.mark.parametrize("sched", [dash.SHIFT, dash.SYMMETRIC_SHIFT])
+def test_two_phase_call_equals_single_call(sched):
+    # dash_attn_bwd_prepare + dash_attn_bwd_run is dash_attn_bwd, bit for bit,
+    # and a workspace can be reused call after call
+    B, S, Hq, Hkv, D, causal = CASES[0]
+    print("two-phase", CASES[0], "schedule", sched, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=2100)
+    o, lse = gu.run_forward(x, causal)
+    ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
+    ref = gu.run_backward(x, o, lse, causal, sched, workspace=ws)
+    ref = [t.clone() for t in ref]
+    dq, dk, dv = (torch.empty_like(t) for t in ref)
+    for _ in range(3):
+        dash.dash_attn_bwd_prepare(o, x["do"], lse, tuple(x["q"].shape), Hkv, int(causal),
+                                   sched, ws)
+        dash.dash_attn_bwd_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, int(causal),
+                               sched, ws)
+        dash.dash_attn_bwd_check(ws)
+        for a, b in zip(ref, (dq, dk, dv)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
