@@ -248,6 +248,23 @@ __device__ __forceinline__ void load_row_vec_async(const float* src, const char*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
 }
 
+// P = exp2(S * scale * log2e - lse * log2e) and dS = P * (dP - Dl) for one
+// 32x32 accumulator block, rounded to bf16 as the B operands of dV and dK.
+// MASKED: elements whose bit is set in zb are forced to P = 0.
+template <bool MASKED>
+__device__ __forceinline__ void softmax_block(const f32x16& sacc, const f32x16& dpacc, const f32x4* l2,
+                                              const f32x4* dl, float scale_log2e, unsigned zb,
+                                              bf16x8* pb, bf16x8* dsb) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float pv = __builtin_amdgcn_exp2f(sacc[r] * scale_log2e - l2[r >> 2][r & 3]);
+    if constexpr (MASKED) pv = ((zb >> r) & 1u) ? 0.0f : pv;
+    const float ds = pv * (dpacc[r] - dl[r >> 2][r & 3]);
+    pb[r >> 3][r & 7] = (bf16)pv;
+    dsb[r >> 3][r & 7] = (bf16)ds;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // A task (KV tile i, Q tile j of T rows) is processed in passes of BQ = 64
 // query rows.  Per pass the Q/dO rows, their lse2/Dl values and the dS block
@@ -290,7 +307,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   char* const lS = smem + C::OFF_DS;
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // (the mask tells the compiler that w < NW, so the loaders need no bounds tests)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & (C::NW - 1);
   const int lane = tid & 63, c = lane & 31, hg = lane >> 5, g16 = lane >> 4, s16 = lane & 15;
   const int qg = w / C::DB, db = w % C::DB;  // this wave's dQ block within a pass
   constexpr int mask = CAUSAL ? MASK_CAUSAL : MASK_FULL;
@@ -334,6 +352,11 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
     const int key = 32 * w + c;
     offW[x] = phys<C::RBS>(row, key >> 3) + 2 * (key & 7);
   }
+  // causal diagonal block: bit r set where key c comes after query row
+  // 8(r >> 2) + 4hg + (r & 3) of the accumulator layout
+  unsigned diag_bits = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) diag_bits |= (c > 8 * (r >> 2) + 4 * hg + (r & 3) ? 1u : 0u) << r;
   // loader: source (row, chunk) of the slot this lane fills in its first block
   int ldRow0, ldChunk0;
   slot_source<C::RBD>(4 * w + (lane >> 4), lane & 15, &ldRow0, &ldChunk0);
@@ -455,17 +478,13 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
             dl[k4] = *reinterpret_cast<const f32x4*>(lDl + 4 * (32 * mt + 8 * k4 + 4 * hg));
           }
           bf16x8 pb[2], dsb[2];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(sacc[r] * p.scale_log2e - l2[r >> 2][r & 3]);
-            if (diag && qb == w) {
-              const int ql = 8 * (r >> 2) + 4 * hg + (r & 3);
-              if (c > ql) pv = 0.0f;
-            }
-            if (kv_tail && !key_ok) pv = 0.0f;
-            const float ds = pv * (dpacc[r] - dl[r >> 2][r & 3]);
-            pb[r >> 3][r & 7] = (bf16)pv;
-            dsb[r >> 3][r & 7] = (bf16)ds;
+          if ((diag && qb == w) || kv_tail) {
+            // bit r of zb: element r is masked (key after query on the
+            // diagonal block, or key past the sequence end)
+            const unsigned zb = ((diag && qb == w) ? diag_bits : 0u) | ((kv_tail && !key_ok) ? 0xffffu : 0u);
+            softmax_block<true>(sacc, dpacc, l2, dl, p.scale_log2e, zb, pb, dsb);
+          } else {
+            softmax_block<false>(sacc, dpacc, l2, dl, p.scale_log2e, 0u, pb, dsb);
           }
           {
             // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows of block mt
