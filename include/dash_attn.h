@@ -95,12 +95,12 @@ int dash_attn_tile_size(int S, int D);
  *   ctrl      64 x int32   [0] work-dispatch counter, [1] watchdog flag,
  *                          [2] number of waits that timed out
  *   counters  B*Hq*N*W int32: the turn counter of every (batch, query head,
- *             dQ tile, slice) -- a slice is one 32-feature or 32-row part of
- *             one 64-row pass over the tile; after a deterministic backward
- *             each holds the number of key/value tiles that reduced into that
- *             dQ tile (N = ceil(S/T), W = T*T/2048)
- *   delta     B*Hq*N*T fp32: rowsum(dO * O), zero past S
- *   lse2      B*Hq*N*T fp32: lse * log2(e), +inf past S
+ *             dQ tile, slice) -- a slice is one 32-row x 32-feature block of
+ *             the tile; after a deterministic backward each holds the number
+ *             of key/value tiles that reduced into that dQ tile
+ *             (N = ceil(S/T), W = T*D/1024)
+ *   delta     B*Hq*N*T fp32: -rowsum(dout * o), zero past S
+ *   lse2      B*Hq*N*T fp32: -lse / scale, -inf past S
  *   dqacc     B*Hq*N*T*D fp32: dQ partial sums in the kernels' lane order
  */
 size_t dash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int S, int D,
@@ -138,10 +138,10 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * them separately (same arguments and checks; pointers a phase does not read
  * may be NULL).
  *
- * dash_attn_bwd_prepare: the per-row preprocessing of the technical summary's
- * section 2.1 -- delta = rowsum(dout * o) and lse * log2(e) into the
- * workspace -- and the reset of the work-dispatch counter, the watchdog flag
- * and every turn counter (and, for ATOMIC, the dQ accumulator).
+ * dash_attn_bwd_prepare: the per-row values of the standard attention
+ * backward -- -rowsum(dout * o) and -lse/scale into the workspace -- and the
+ * reset of the work-dispatch counter, the watchdog flag and every turn
+ * counter (and, for ATOMIC, the dQ accumulator).
  *
  * dash_attn_bwd_run: the persistent backward over the schedule's items (and,
  * for ATOMIC, the pass that converts the fp32 accumulator to bf16 dq).  It

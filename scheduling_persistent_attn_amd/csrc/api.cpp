@@ -73,8 +73,8 @@ int make_layout(int B, int Hq, int S, int D, Layout* L) {
   L->T = dash_attn_tile_size(S, D);
   if (L->T == 0) return DASH_ERR_UNSUPPORTED;
   L->N = (S + L->T - 1) / L->T;
-  // one turn counter per (dQ tile, 64-row pass, wave): T/64 * T/32 per tile
-  L->NW = (L->T / 64) * (L->T / 32);
+  // one turn counter per 32x32 slice of a dQ tile: T*D/1024 per tile
+  L->NW = L->T * D / 1024;
   const long long rows = (long long)B * Hq * L->N * L->T;
   L->n_rows = rows;
   L->n_counters = (long long)B * Hq * L->N * L->NW;
@@ -231,6 +231,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   pp.n_counters = L.n_counters;
   pp.n_dqacc = L.n_dqacc;
   pp.zero_dqacc = schedule == DASH_SCHED_ATOMIC;
+  pp.inv_scale = (float)__builtin_sqrt((double)D);
   pp.B = B;
   pp.Hq = Hq;
   pp.S = S;

@@ -1,8 +1,9 @@
 // Deterministic attention backward for gfx950 (CDNA4).
 //
 // Kernels:
-//   bwd_preprocess   Dl = rowsum(dO * O), lse2 = lse * log2(e) (padded to whole
-//                    tiles), zeroing of the turn counters and dispatch state.
+//   bwd_preprocess   per query row: -Dl = -rowsum(dO * O) and -lse/scale
+//                    (padded to whole tiles with 0 and -inf), zeroing of the
+//                    turn counters and dispatch state.
 //   bwd_main         persistent backward: one workgroup per compute unit takes
 //                    items (a key/value chain, or a symmetric pair of chains)
 //                    from a device-wide counter and runs them tile by tile.
@@ -13,28 +14,27 @@
 // key/value tile stay in registers while one unit walks that tile's query
 // tiles; each query tile's dQ is reduced across key/value tiles in a fixed
 // order.  Here the fixed order is enforced with one turn counter per
-// (query head, dQ tile, wave slice): the reduction of rank r waits until the
-// counter equals r, adds its partial into the fp32 accumulator in HBM, then
-// publishes r + 1 (agent-scope release/acquire, so the hand-off also works
-// between the eight XCDs, whose L2 caches are not coherent with each other).
+// (query head, dQ tile, pass, wave slice): the reduction of rank r waits until
+// the counter equals r, adds its partial into the fp32 accumulator in HBM,
+// then publishes r + 1 (agent-scope, so the hand-off also works between the
+// eight XCDs, whose L2 caches are not coherent with each other).
 //
 // Workgroup = T/32 waves; wave w owns keys [32w, 32w+32) of the key/value tile.
-// Per task (KV tile i, Q tile j, query head h), per 32-row block mt of Q:
-//   S    = Q K^T          A = Q rows (LDS),   B = K fragments (registers)
-//   dP   = dO V^T         A = dO rows (LDS),  B = V fragments (registers)
-//   P    = exp2(S*scale*log2e - lse*log2e),  dS = P * (dP - Dl)
-//   dV^T += dO^T P        A = dO^T (LDS, transposed copy), B = P (registers)
-//   dK^T += Q^T dS        A = Q^T  (LDS, transposed copy), B = dS (registers)
+// Per task (KV tile i, Q tile j, query head h), per 32-row block of Q:
+//   S - lse/scale = Q K^T  (accumulator starts at -lse/scale; A = Q rows, B = K rows)
+//   dP - Dl       = dO V^T (accumulator starts at -Dl; B = V rows in registers)
+//   P = exp2((S - lse/scale) * scale * log2e),  dS = P * (dP - Dl)
+//   dV^T += dO^T P        A = dO^T (transposing LDS reads), B = P (registers)
+//   dK^T += Q^T dS        A = Q^T  (transposing LDS reads), B = dS (registers)
 //   dS -> LDS
-// then per wave a 32-column slice of dQ = dS K with A = dS (LDS) and B = K^T
-// fragments (registers), followed by the ordered reduction.
+// and per wave a 32-column slice of dQ = dS K with A = dS (LDS) and B = K^T
+// (transposing LDS reads), followed by the ordered reduction.
 // All products use v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulate).
 // The 32x32 accumulator holds column n = lane % 32 and rows
 // 8*(r/4) + 4*(lane/32) + r%4 in register r; a product whose contraction runs
 // over those rows takes the accumulator (converted to bf16) directly as its B
 // operand, provided its A operand enumerates the contraction index in the same
-// permuted order -- which the transposed LDS copies provide with two 8-byte
-// reads.
+// permuted order -- which the transposing LDS reads provide.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -49,8 +49,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -132,7 +130,9 @@ __device__ __forceinline__ bf16x8 lds_read_tr(const char* base, int off0, int of
 
 // ---------------------------------------------------------------------------
 // Preprocess.  One row (b, h, s) of Dl per D/8 lanes; lanes reduce their
-// 8-element partial dot products with a fixed butterfly.
+// 8-element partial dot products with a fixed butterfly.  Stores the values
+// the main kernel's accumulators start from: -Dl, and -lse/scale (rows past
+// S: 0 and -inf, so that P = 0 there).
 __global__ __launch_bounds__(256) void bwd_preprocess(PreParams p) {
   const int lpr = p.D / 8;
   const int rows_per_block = 256 / lpr;
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess(PreParams p) {
   }
   for (int m = lpr / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (row < nrows && sub == 0) {
-    p.delta[row] = acc;
-    p.lse2[row] = s < p.S ? p.lse[bh * p.S + s] * kLog2e : __builtin_inff();
+    p.delta[row] = -acc;
+    p.lse2[row] = s < p.S ? -p.lse[bh * p.S + s] * p.inv_scale : -__builtin_inff();
   }
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long nthreads = (long long)gridDim.x * blockDim.x;
@@ -241,70 +241,333 @@ __device__ __forceinline__ void load_tile_async(const bf16* g, int rs, int nvali
   }
 }
 
-// Asynchronous copy of 64 consecutive floats (a row range of the padded
-// lse2 / Dl arrays) into LDS: one dword load of 64 lanes.
+// Asynchronous copy of N (32 or 64) consecutive floats (a row range of the
+// padded -lse/scale or -Dl arrays) into LDS: one dword load, lane l -> float l.
+template <int N>
 __device__ __forceinline__ void load_row_vec_async(const float* src, const char* dst, int lane) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, 256, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
-}
-
-// P = exp2(S * scale * log2e - lse * log2e) and dS = P * (dP - Dl) for one
-// 32x32 accumulator block, rounded to bf16 as the B operands of dV and dK.
-// MASKED: elements whose bit is set in zb are forced to P = 0.
-template <bool MASKED>
-__device__ __forceinline__ void softmax_block(const f32x16& sacc, const f32x16& dpacc, const f32x4* l2,
-                                              const f32x4* dl, float scale_log2e, unsigned zb,
-                                              bf16x8* pb, bf16x8* dsb) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float pv = __builtin_amdgcn_exp2f(sacc[r] * scale_log2e - l2[r >> 2][r & 3]);
-    if constexpr (MASKED) pv = ((zb >> r) & 1u) ? 0.0f : pv;
-    const float ds = pv * (dpacc[r] - dl[r >> 2][r & 3]);
-    pb[r >> 3][r & 7] = (bf16)pv;
-    dsb[r >> 3][r & 7] = (bf16)ds;
-  }
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, 4 * N, 0x00020000);
+  if (N == 64 || lane < N) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// A task (KV tile i, Q tile j of T rows) is processed in passes of BQ = 64
-// query rows.  Per pass the Q/dO rows, their lse2/Dl values and the dS block
-// are BQ rows; the K and V tiles (T rows) stay in LDS for the whole run of the
-// KV tile.  Q/dO/lse2/Dl are double-buffered: the next pass is copied into
-// LDS while the current one computes.
+// A task (KV tile i, Q tile j of T rows) is processed in passes of BQ query
+// rows: QBP blocks of 32 rows, with BQ chosen so that the pass's dQ (BQ x D)
+// splits into one 32 x 32 block per wave.  The operands a wave needs from its
+// KV tile stay in registers for the whole run of the tile: the K and V rows
+// it owns (B operands of S and dP) and the K^T fragments of its dQ feature
+// block (B operand of dQ = dS K); the K tile passes through LDS once per run
+// to form them.  Q/dO and the per-row -lse/scale, -Dl values of a pass are
+// double-buffered in LDS (the next pass is copied in while the current one
+// computes), and so is dS: the dQ product of pass p-1, which needs every
+// wave's dS, runs during pass p next to that pass's softmax, so one workgroup
+// barrier per pass suffices and the matrix cores have independent work while
+// the vector units evaluate exp2.  The ordered reduction of pass p-1's slice
+// is spread over pass p: its turn counter is polled at the start, the
+// accumulator loads are issued after the first products and the add and
+// store come at the end, so the round trips to the device-coherent level
+// overlap with computation.  The last pass of a KV tile's run finishes its
+// own dQ and reduction before the tile changes.
 template <int D, int T, bool CAUSAL>
 struct BwdCfg {
-  static constexpr int BQ = 64;          // query rows per pass
-  static constexpr int NP = T / BQ;      // passes per task
   static constexpr int NW = T / 32;      // waves; wave w owns keys [32w, 32w+32)
+  static constexpr int DB = D / 32;      // 32-wide feature blocks
+  static constexpr int QBP = NW / DB;    // 32-row blocks per pass
+  static constexpr int BQ = 32 * QBP;    // query rows per pass
+  static constexpr int NP = T / BQ;      // passes per task
   static constexpr int KBD = D / 16;     // k-blocks over the head dim
   static constexpr int KBT = T / 16;     // k-blocks over a tile of keys
-  static constexpr int DB = D / 32;      // 32-wide feature blocks
-  static constexpr int QBP = BQ / 32;    // 32-row blocks per pass
-  static constexpr int MQ = QBP * DB / NW;  // dQ row blocks per wave and pass
-  static constexpr int RBD = 2 * D;      // bytes per row of a Q/dO/K/V tile
+  static constexpr int RBD = 2 * D;      // bytes per row of a Q/dO/K tile
   static constexpr int RBS = 2 * T;      // bytes per row of the dS block
-  static constexpr int KV_TILE = T * RBD, Q_TILE = BQ * RBD;
-  static constexpr int OFF_K = 0, OFF_V = KV_TILE;
-  static constexpr int OFF_Q = 2 * KV_TILE;            // + buf * Q_TILE
+  static constexpr int K_TILE = T * RBD, Q_TILE = BQ * RBD, S_TILE = BQ * RBS;
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_Q = K_TILE;                 // + buf * Q_TILE
   static constexpr int OFF_DO = OFF_Q + 2 * Q_TILE;    // + buf * Q_TILE
-  static constexpr int OFF_DS = OFF_DO + 2 * Q_TILE;
-  static constexpr int OFF_LD = OFF_DS + BQ * RBS;     // [buf][lse2 | Dl][BQ] fp32
-  static constexpr int LDS_BYTES = OFF_LD + 2 * 2 * 4 * BQ;
-  static_assert(T >= D && T % BQ == 0, "tile must be at least the head dim");
-  static_assert(MQ >= 1 && (QBP * DB) % NW == 0, "dQ work split");
+  static constexpr int OFF_DS = OFF_DO + 2 * Q_TILE;   // + buf * S_TILE
+  static constexpr int OFF_LD = OFF_DS + 2 * S_TILE;   // [buf][-lse/scale | -Dl][BQ] fp32
+  static constexpr int OFF_MISC = OFF_LD + 2 * 2 * 4 * BQ;
+  static constexpr int LDS_BYTES = OFF_MISC + 16;
+  static_assert(T >= D && NW % DB == 0 && T % BQ == 0, "tile shape");
   static_assert(RBD == 128 || RBD == 256, "head dim 64 or 128");
   static_assert(RBS == 128 || RBS == 256, "tile 64 or 128");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+
+// Per-lane LDS byte offsets.  The swizzle XORs a function of the row's low
+// bits into the 16-byte slot index, and every access pattern of the kernel
+// varies the slot index only in bits that this function leaves alone or in
+// whole 16-row steps, so each pattern is one per-lane base XOR a constant (or
+// plus a constant multiple of 16 rows, which the instruction's immediate
+// offset absorbs).  Only the bases are kept in registers.
+template <int D, int T>
+struct LaneOffs {
+  int a;      // 16-byte row reads of Q/dO/K: row c, chunk 2kb + hg is a ^ 32kb
+  int s;      // 16-byte row reads of dS: row c, chunk 2kb + hg is s ^ 32kb
+  int tq[2];  // transposing reads of Q/dO rows 8h8 + 4hg + (s16 >> 2), feature
+              // block md: tq[h8] ^ 64md
+  int kt[2];  // transposing reads of K rows 8hg + 4h4 + (s16 >> 2), features of
+              // block db (+16kb rows: immediate offset)
+  int wr;     // dS element writes of row 8(x >> 2) + 4hg + (x & 3), key 32w + c:
+              // (wr ^ wx(x)) + wy(x)
+  __device__ __forceinline__ int A(int kb) const { return a ^ (32 * kb); }
+  __device__ __forceinline__ int S(int kb) const { return s ^ (32 * kb); }
+  __device__ __forceinline__ int Tq(int md, int h8) const { return tq[h8] ^ (64 * md); }
+  // constant parts of the dS write address of element x (see wr)
+  static constexpr int wx(int x) {
+    return T == 128 ? ((((x & 3) << 1) ^ ((x & 3) << 2) ^ (2 * (x >> 2))) << 4)
+                    : ((8 * (x & 1) ^ 6 * ((x >> 1) & 1) ^ ((x >> 2) & 1)) << 4);
+  }
+  static constexpr int wy(int x) {
+    return T == 128 ? (8 * (x >> 2) + (x & 3)) * 256 : (4 * (x >> 2) + ((x >> 1) & 1)) * 256;
+  }
+  __device__ __forceinline__ int W(int x) const { return (wr ^ wx(x)) + wy(x); }
+};
+
+// One wave's 32 x 32 slice of one pass of a dQ tile, and where it goes.
+struct Slice {
+  float* acc;      // fp32 accumulator of the slice (1024 floats)
+  int* cnt;        // its turn counter
+  int rank;        // position of this contribution in the tile's order
+  int last;        // last contributor: writes bf16 dQ instead of the accumulator
+  int dq_off;      // dq element of (slice row 0, feature 32*db + c)
+  int rows_left;   // rows of the slice that exist: query rows < S, minus 1
+};
+
+// P = exp2((S - lse/scale) * scale * log2e) and dS = P * (dP - Dl), with the
+// accumulators already holding S - lse/scale and dP - Dl (masked elements
+// start at -inf, so P = 0 there); rounded to bf16 as the B operands of dV and
+// dK.
+__device__ __forceinline__ void softmax_block(const f32x16& sacc, const f32x16& dpacc, float scale_log2e,
+                                              bf16x8* pb, bf16x8* dsb) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float pv = __builtin_amdgcn_exp2f(sacc[r] * scale_log2e);
+    pb[r >> 3][r & 7] = (bf16)pv;
+    dsb[r >> 3][r & 7] = (bf16)(pv * dpacc[r]);
+  }
+}
+
+// This wave's dQ slice for one pass: 32 rows (block qg) x 32 features (block
+// db), A = dS rows (LDS), B = K^T (transposing reads of the resident K tile).
+template <int D, int T, bool CAUSAL>
+__device__ __forceinline__ f32x16 dq_products(const char* lS, const char* lK, const LaneOffs<D, T>& o,
+                                              int qg) {
+  using C = BwdCfg<D, T, CAUSAL>;
+  f32x16 dq = {};
+  const int row0 = 32 * qg * C::RBS;
+  bf16x8 fa[2], fb[2];
+  fa[0] = lds_read16(lS, o.S(0) + row0);
+  fb[0] = lds_read_tr(lK, o.kt[0], o.kt[1]);
+#pragma unroll
+  for (int kb = 0; kb < C::KBT; ++kb) {
+    if (kb + 1 < C::KBT) {
+      fa[(kb + 1) & 1] = lds_read16(lS, o.S(kb + 1) + row0);
+      fb[(kb + 1) & 1] = lds_read_tr(lK, o.kt[0] + 16 * (kb + 1) * C::RBD, o.kt[1] + 16 * (kb + 1) * C::RBD);
+    }
+    dq = mfma(fa[kb & 1], fb[kb & 1], dq);
+  }
+  return dq;
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows of block m of the
+// pass, fragments one step ahead.
+template <int D, int T, bool CAUSAL>
+__device__ __forceinline__ void dvdk_block(const char* lQ, const char* lO, const LaneOffs<D, T>& o, int m,
+                                           const bf16x8* pb, const bf16x8* dsb, f32x16* dK, f32x16* dV) {
+  using C = BwdCfg<D, T, CAUSAL>;
+  bf16x8 fa[2], fb[2];
+  fa[0] = lds_read_tr(lO, o.Tq(0, 0) + 32 * m * C::RBD, o.Tq(0, 1) + 32 * m * C::RBD);
+  fb[0] = lds_read_tr(lQ, o.Tq(0, 0) + 32 * m * C::RBD, o.Tq(0, 1) + 32 * m * C::RBD);
+#pragma unroll
+  for (int x = 0; x < 2 * C::DB; ++x) {
+    const int md = x >> 1, kq = x & 1;
+    if (x + 1 < 2 * C::DB) {
+      const int md1 = (x + 1) >> 1, kq1 = (x + 1) & 1;
+      const int base = (32 * m + 16 * kq1) * C::RBD;
+      fa[(x + 1) & 1] = lds_read_tr(lO, o.Tq(md1, 0) + base, o.Tq(md1, 1) + base);
+      fb[(x + 1) & 1] = lds_read_tr(lQ, o.Tq(md1, 0) + base, o.Tq(md1, 1) + base);
+    }
+    dV[md] = mfma(fa[x & 1], pb[kq], dV[md]);
+    dK[md] = mfma(fb[x & 1], dsb[kq], dK[md]);
+  }
+}
+
+// Accumulator loads of a slice (device-coherent): element r of lane l at
+// float (r / 4) * 256 + 4 * l + r % 4, i.e. four fully coalesced 1 KB rows.
+// With nbytes = 0 every load is out of range and returns zeros (used when
+// there is no partial sum to add).
+__device__ __forceinline__ void acc_load(float* acc, int nbytes, int lane, f32x4* old) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(acc, 0, nbytes, 0x00020000);
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) old[q4] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + q4 * 1024, 0, kSC1);
+}
+
+// Second half of a slice's reduction: dq + old (the loaded partial sum, zero
+// for rank 0), then store the new partial sum, or for the last contributor
+// write dQ = scale * sum in bf16.  ATOMIC: unordered fp32 atomics instead.
+template <bool ATOMIC>
+__device__ __forceinline__ void acc_finish(const Slice& sl, f32x16 dq, int lane, int hg, int rs, float scale,
+                                           bf16* gdq) {
+  // rs is modified only by an empty asm statement below
+  if constexpr (ATOMIC) {
+    // element r of lane l at r*64 + l: each atomic instruction covers 64
+    // consecutive floats
+#pragma unroll
+    for (int r = 0; r < 16; ++r) unsafeAtomicAdd(sl.acc + r * 64 + lane, dq[r]);
+    return;
+  } else {
+    if (!sl.last) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(sl.acc, 0, 4096, 0x00020000);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 x = {dq[4 * q4], dq[4 * q4 + 1], dq[4 * q4 + 2], dq[4 * q4 + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(x, r, lane * 16 + q4 * 1024, 0, kSC1);
+      }
+    } else if (sl.rows_left >= 31) {
+      asm volatile("" : "+s"(rs));  // keeps the row offsets from being hoisted out of the loop
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = 8 * (r >> 2) + 4 * hg + (r & 3);
+        gdq[sl.dq_off + ql * rs] = (bf16)(dq[r] * scale);
+      }
+    } else {
+      // partial last tile: rows past S are not written
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = 8 * (r >> 2) + 4 * hg + (r & 3);
+        const int qc = min(ql, max(sl.rows_left, 0));
+        const bf16 v = (bf16)(dq[r] * scale);
+        if (ql <= sl.rows_left) gdq[sl.dq_off + qc * rs] = v;
+      }
+    }
+  }
+}
+
+// Publishes rank + 1 on a slice's counter.  The caller has waited for this
+// wave's accumulator stores (s_waitcnt) before.
+__device__ __forceinline__ void release(const Slice& sl, int lane) {
+  if (lane == 0) __hip_atomic_store(sl.cnt, sl.rank + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Blocks until *cnt equals expect, given a first poll result; the
+// accumulator loads follow the acquire point.
+__device__ __forceinline__ void acquire(const int* cnt, int expect, int polled, int* ctrl, long long spin_ticks,
+                                        int lane) {
+  if (__builtin_amdgcn_readfirstlane(polled) != expect) wait_turn(cnt, expect, ctrl, spin_ticks, lane);
+  order_point();
+}
+
+// One pass of the current task, plus two stages of the ordered reductions of
+// earlier passes:
+//   * slice `fin` (two passes back), whose dQ partial dq_fin and loaded
+//     partial sum old_fin the previous pass left in registers: added and
+//     stored (or, for the last contributor, written to dq) after the S/dP
+//     products, when fin_on;
+//   * slice `prev` (the previous pass): its turn, polled at the start of the
+//     pass, is checked after the S/dP products, then its accumulator loads are
+//     issued (zeros when there is no partial sum to add) and its dQ product
+//     is formed from lS_prev; both are returned in dq_fin / old_fin for the
+//     next pass.  (Without a previous pass the product is formed and
+//     dropped.)
+// The loads thus have a whole pass to arrive, and the stores a whole pass to
+// complete before the counter is bumped after the next barrier.  The code
+// from the acquire to the end has no branches, so that the compiler can
+// interleave the softmax with the dQ and dV/dK products.  Writes dS of this
+// pass into lS_cur.  When masked, elements with their bit set in zb[m] start
+// at -inf (P = 0).
+template <int D, int T, bool CAUSAL, bool ATOMIC>
+__device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const char* lL, const char* lK,
+                                          char* lS_cur, const char* lS_prev, const LaneOffs<D, T>& o, int qg,
+                                          int hg, int lane, float scale_log2e, bool masked, const unsigned* zb,
+                                          const bf16x8* fk, const bf16x8* vB, f32x16* dK, f32x16* dV,
+                                          const Slice& fin, bool fin_on, f32x16& dq_fin, f32x4* old_fin,
+                                          const Slice& prev, const int* poll_ptr, int poll_expect, int polled,
+                                          int acc_bytes, const BwdParams& p, int rs, bf16* gdq) {
+  using C = BwdCfg<D, T, CAUSAL>;
+  constexpr int QBP = C::QBP;
+  // ---- S and dP of the pass's 32-row blocks; the accumulators start at
+  // -lse/scale and -Dl of their rows (rows 8(r/4) + 4hg + r%4)
+  f32x16 sa[QBP], pa[QBP];
+#pragma unroll
+  for (int m = 0; m < QBP; ++m)
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const f32x4 l = *reinterpret_cast<const f32x4*>(lL + 4 * (32 * m + 8 * k4 + 4 * hg));
+      const f32x4 d = *reinterpret_cast<const f32x4*>(lL + 4 * C::BQ + 4 * (32 * m + 8 * k4 + 4 * hg));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa[m][4 * k4 + e] = l[e];
+        pa[m][4 * k4 + e] = d[e];
+      }
+    }
+  if (masked) {
+#pragma unroll
+    for (int m = 0; m < QBP; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[m][r] = ((zb[m] >> r) & 1u) ? -__builtin_inff() : sa[m][r];
+  }
+  {
+    bf16x8 fq[2][QBP], fd[2][QBP];
+#pragma unroll
+    for (int m = 0; m < QBP; ++m) {
+      fq[0][m] = lds_read16(lQ, o.A(0) + 32 * m * C::RBD);
+      fd[0][m] = lds_read16(lO, o.A(0) + 32 * m * C::RBD);
+    }
+#pragma unroll
+    for (int kb = 0; kb < C::KBD; ++kb) {
+      const int n = (kb + 1) & 1;
+      if (kb + 1 < C::KBD) {
+#pragma unroll
+        for (int m = 0; m < QBP; ++m) {
+          fq[n][m] = lds_read16(lQ, o.A(kb + 1) + 32 * m * C::RBD);
+          fd[n][m] = lds_read16(lO, o.A(kb + 1) + 32 * m * C::RBD);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < QBP; ++m) {
+        sa[m] = mfma(fq[kb & 1][m], fk[kb], sa[m]);
+        pa[m] = mfma(fd[kb & 1][m], vB[kb], pa[m]);
+      }
+    }
+  }
+
+  // ---- the slice of two passes back: add and store
+  if (fin_on) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dq_fin[4 * q4 + e] = old_fin[q4][e] + dq_fin[4 * q4 + e];
+    acc_finish<ATOMIC>(fin, dq_fin, lane, hg, rs, p.scale, gdq);
+  }
+
+  // ---- turn of the previous slice, then its accumulator loads (zeros when
+  // there is nothing to add)
+  if constexpr (!ATOMIC) acquire(poll_ptr, poll_expect, polled, p.ctrl, p.spin_ticks, lane);
+  acc_load(prev.acc, acc_bytes, lane, old_fin);
+
+  // ---- softmax next to the dQ product of the previous pass
+  bf16x8 pb[QBP][2], dsb[QBP][2];
+#pragma unroll
+  for (int m = 0; m < QBP; ++m) softmax_block(sa[m], pa[m], scale_log2e, pb[m], dsb[m]);
+  dq_fin = dq_products<D, T, CAUSAL>(lS_prev, lK, o, qg);
+
+  // ---- dV^T += dO^T P, dK^T += Q^T dS; dS -> LDS
+#pragma unroll
+  for (int m = 0; m < QBP; ++m) {
+    dvdk_block<D, T, CAUSAL>(lQ, lO, o, m, pb[m], dsb[m], dK, dV);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      *reinterpret_cast<bf16*>(lS_cur + o.W(r & 7) + (r >> 3) * 16 * C::RBS + 32 * m * C::RBS) =
+          dsb[m][r >> 3][r & 7];
+  }
+}
 
 template <int D, int T, bool CAUSAL, int SCHED>
 __global__ __attribute__((amdgpu_flat_work_group_size(2 * T, 2 * T)))
 __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   using C = BwdCfg<D, T, CAUSAL>;
-  constexpr int BQ = C::BQ, NP = C::NP;
+  constexpr int BQ = C::BQ, NP = C::NP, QBP = C::QBP;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   const char* const lK = smem + C::OFF_K;
-  const char* const lV = smem + C::OFF_V;
-  char* const lS = smem + C::OFF_DS;
 
   const int tid = threadIdx.x;
   // (the mask tells the compiler that w < NW, so the loaders need no bounds tests)
@@ -314,44 +577,29 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   constexpr int mask = CAUSAL ? MASK_CAUSAL : MASK_FULL;
   constexpr bool atomic_dq = SCHED == SCHED_ATOMIC;
   const int N = p.N, G = p.G, S = p.S;
+  const int rsq = p.Hq * D;  // row stride of q / dout / dq
+  bf16* const gdq = (bf16*)p.dq;
 
-  // ---- per-lane LDS offsets, computed once ---------------------------------
-  // 16-byte row reads: row c, chunk 2kb + hg (A fragments of S and dP from
-  // Q/dO; B fragments from K/V rows 32w + c)
-  int offA[C::KBD];
+  // ---- per-lane LDS offsets ------------------------------------------------
+  LaneOffs<D, T> o;
+  o.a = phys<C::RBD>(c, hg);
+  o.s = phys<C::RBS>(c, hg);
+  // transposing reads of Q / dO: source lane s16 reads row 4hg + (s16 >> 2)
+  // (+8 for the upper half), features 16(g16 & 1) + 4(s16 & 3) .. +3 of block 0
 #pragma unroll
-  for (int kb = 0; kb < C::KBD; ++kb) offA[kb] = phys<C::RBD>(c, 2 * kb + hg);
-  // transposing reads of Q / dO for the A fragments of dK^T and dV^T:
-  // source lane s16 reads row 4hg + (s16 >> 2) (+8 for the upper half),
-  // features 32md + 16(g16 & 1) + 4(s16 & 3) .. +3
-  int offT[C::DB][2];
-#pragma unroll
-  for (int md = 0; md < C::DB; ++md)
-#pragma unroll
-    for (int h8 = 0; h8 < 2; ++h8) {
-      const int col = 32 * md + 16 * (g16 & 1) + 4 * (s16 & 3);
-      offT[md][h8] = phys<C::RBD>(8 * h8 + 4 * hg + (s16 >> 2), col >> 3) + 2 * (col & 7);
-    }
-  // transposing reads of K for the B fragments of dQ = dS K: keys
-  // 8hg + 4h4 + (s16 >> 2) of each 16-key block, features of block db
-  int offK[2];
+  for (int h8 = 0; h8 < 2; ++h8) {
+    const int col = 16 * (g16 & 1) + 4 * (s16 & 3);
+    o.tq[h8] = phys<C::RBD>(8 * h8 + 4 * hg + (s16 >> 2), col >> 3) + 2 * (col & 7);
+  }
+  // transposing reads of K for dQ = dS K: keys 8hg + 4h4 + (s16 >> 2) of each
+  // 16-key block, features of block db
 #pragma unroll
   for (int h4 = 0; h4 < 2; ++h4) {
     const int col = 32 * db + 16 * (g16 & 1) + 4 * (s16 & 3);
-    offK[h4] = phys<C::RBD>(8 * hg + 4 * h4 + (s16 >> 2), col >> 3) + 2 * (col & 7);
+    o.kt[h4] = phys<C::RBD>(8 * hg + 4 * h4 + (s16 >> 2), col >> 3) + 2 * (col & 7);
   }
-  // A fragments of dQ: dS row c, chunk 2kb + hg
-  int offS[C::KBT];
-#pragma unroll
-  for (int kb = 0; kb < C::KBT; ++kb) offS[kb] = phys<C::RBS>(c, 2 * kb + hg);
-  // dS element writes: row 8((r >> 2) & 1) + 4hg + (r & 3), key 32w + c
-  int offW[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int row = 8 * (x >> 2) + 4 * hg + (x & 3);
-    const int key = 32 * w + c;
-    offW[x] = phys<C::RBS>(row, key >> 3) + 2 * (key & 7);
-  }
+  // dS element writes: key 32w + c, row 4hg (+ the per-element constants)
+  o.wr = phys<C::RBS>(4 * hg, (32 * w + c) >> 3) + 2 * ((32 * w + c) & 7);
   // causal diagonal block: bit r set where key c comes after query row
   // 8(r >> 2) + 4hg + (r & 3) of the accumulator layout
   unsigned diag_bits = 0;
@@ -362,40 +610,50 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   slot_source<C::RBD>(4 * w + (lane >> 4), lane & 15, &ldRow0, &ldChunk0);
 
   f32x16 dK[C::DB], dV[C::DB];
+  // operands from the current KV tile, held for its whole run (dQ reads K^T
+  // from the resident K tile):
+  bf16x8 fk[C::KBD];   // K rows 32w + c (B operand of S)
+  bf16x8 vB[C::KBD];   // V rows 32w + c (B operand of dP)
 
-  // Q, dO, lse2, Dl of rows [j*T + hp*BQ, +BQ) of head h into buffer buf
+  // Q, dO, -lse/scale, -Dl of rows [j*T + hp*BQ, +BQ) of head h into buffer buf
 #define LOAD_PASS(b_, h_, j_, hp_, buf_)                                                     \
   do {                                                                                       \
-    const int rs_ = p.Hq * D;                                                                \
     const int r0_ = (j_) * T + (hp_) * BQ;                                                   \
     const int off_ = (((b_) * S + r0_) * p.Hq + (h_)) * D;                                   \
-    load_tile_async<D, BQ, C::NW>((const bf16*)p.q + off_, rs_, S - r0_,                     \
+    load_tile_async<D, BQ, C::NW>((const bf16*)p.q + off_, rsq, S - r0_,                     \
                                   smem + C::OFF_Q + (buf_) * C::Q_TILE, w, ldRow0, ldChunk0); \
-    load_tile_async<D, BQ, C::NW>((const bf16*)p.dout + off_, rs_, S - r0_,                  \
+    load_tile_async<D, BQ, C::NW>((const bf16*)p.dout + off_, rsq, S - r0_,                  \
                                   smem + C::OFF_DO + (buf_) * C::Q_TILE, w, ldRow0, ldChunk0); \
     const int row0_ = (((b_) * p.Hq + (h_)) * N + (j_)) * T + (hp_) * BQ;                    \
     if (w < 2)                                                                               \
-      load_row_vec_async((w == 0 ? p.lse2 : p.delta) + row0_,                                \
-                         smem + C::OFF_LD + ((buf_) * 2 + w) * 4 * BQ, lane);                \
+      load_row_vec_async<BQ>((w == 0 ? p.lse2 : p.delta) + row0_,                            \
+                             smem + C::OFF_LD + ((buf_) * 2 + w) * 4 * BQ, lane);            \
   } while (0)
 
-  int gp = 0;  // passes processed by this workgroup (selects the buffer)
+  int gp = 0;        // passes processed by this workgroup (selects the buffers)
+  // reduction pipeline: prev = slice of the previous pass (dS in LDS), fin =
+  // slice whose dQ partial and loaded partial sum are in dq_fin / old_fin,
+  // rel = slice whose stores are issued but whose counter is not yet bumped
+  Slice prev = {}, fin = {}, rel = {};
+  bool have_prev = false, have_fin = false, rel_pending = false;
+  f32x16 dq_fin = {};
+  f32x4 old_fin[4] = {};
   for (;;) {
     __syncthreads();  // previous item's LDS use complete
+    int* const misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
     if (tid == 0) {
       int it = atomicAdd(p.ctrl, 1);
       if (__hip_atomic_load(p.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
         it = p.total_items;
-      reinterpret_cast<int*>(lS)[0] = it;
+      misc[0] = it;
     }
     __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(lS)[0]);
+    const int item = __builtin_amdgcn_readfirstlane(misc[0]);
     if (item >= p.total_items) break;
     const int grp = item / p.items_per_group;
     const int local = item - grp * p.items_per_group;
     const int b = grp / p.Hkv, hk = grp - b * p.Hkv;
     const int len = item_len(mask, SCHED, N, G, local);
-    __syncthreads();  // everyone has read the item index held in lS
     {
       const Task t0 = task_at(mask, SCHED, N, G, local, 0);
       LOAD_PASS(b, hk * G + t0.g, t0.j, 0, gp & 1);
@@ -405,33 +663,81 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
       const Task t = task_at(mask, SCHED, N, G, local, step);
       const int i = t.i, j = t.j, h = hk * G + t.g;
       if (t.seg_begin) {
-        __syncthreads();  // the K/V tiles of the previous segment are no longer read
+        // new KV tile: K through LDS into this wave's K and K^T fragments, V
+        // rows straight into registers
+        __syncthreads();  // the K tile of the previous run is no longer read
         const int rs = p.Hkv * D;
         const int off = ((b * S + i * T) * p.Hkv + hk) * D;
-        load_tile_async<D, T, C::NW>((const bf16*)p.k + off, rs, S - i * T, lK, w, ldRow0, ldChunk0);
-        load_tile_async<D, T, C::NW>((const bf16*)p.v + off, rs, S - i * T, lV, w, ldRow0, ldChunk0);
+        load_tile_async<D, T, C::NW>((const bf16*)p.k + off, rs, S - i * T, smem + C::OFF_K, w, ldRow0,
+                                     ldChunk0);
+        {
+          const int nv = S - i * T;
+          const int nbytes = nv <= 0 ? 0 : ((nv - 1) * rs + D) * 2;
+          const __amdgpu_buffer_rsrc_t rv =
+              __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)p.v + off), 0, nbytes, 0x00020000);
+#pragma unroll
+          for (int kb = 0; kb < C::KBD; ++kb) {
+            const f32x4 x =
+                __builtin_amdgcn_raw_buffer_load_b128(rv, ((32 * w + c) * rs + 16 * kb + 8 * hg) * 2, 0, 0);
+            vB[kb] = __builtin_bit_cast(bf16x8, x);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // the K tile is in LDS
+#pragma unroll
+        for (int kb = 0; kb < C::KBD; ++kb) fk[kb] = lds_read16(lK, o.A(kb) + 32 * w * C::RBD);
+        // the held fragments live in the accumulation registers (MFMA takes
+        // its B operand from there), leaving the vector registers to the
+        // per-pass work
+#pragma unroll
+        for (int kb = 0; kb < C::KBD; ++kb) asm volatile("" : "+a"(fk[kb]), "+a"(vB[kb]));
 #pragma unroll
         for (int md = 0; md < C::DB; ++md) {
           dK[md] = f32x16{};
           dV[md] = f32x16{};
         }
       }
-      const bool diag = CAUSAL && i == j;
       const bool kv_tail = (i + 1) * T > S;
       const int key_local = 32 * w + c;
       const bool key_ok = i * T + key_local < S;
+      const bool masked = (CAUSAL && i == j) || kv_tail;
+      const int tile = (b * p.Hq + h) * N + j;
+      const int ncontrib = contributors(mask, N, j);
 
       for (int hp = 0; hp < NP; ++hp, ++gp) {
         const int buf = gp & 1;
         const char* const lQ = smem + C::OFF_Q + buf * C::Q_TILE;
         const char* const lO = smem + C::OFF_DO + buf * C::Q_TILE;
         const char* const lL = smem + C::OFF_LD + buf * 2 * 4 * BQ;
-        const char* const lDl = lL + 4 * BQ;
+        char* const lS_cur = smem + C::OFF_DS + buf * C::S_TILE;
+        const char* const lS_prev = smem + C::OFF_DS + (buf ^ 1) * C::S_TILE;
+        // re-materialise the offset bases each pass, so that the compiler
+        // derives the per-access offsets here instead of keeping dozens of
+        // them alive across the loop
+        asm volatile("" : "+v"(o.a), "+v"(o.s), "+v"(o.tq[0]), "+v"(o.tq[1]), "+v"(o.kt[0]), "+v"(o.kt[1]),
+                     "+v"(o.wr));
+        // and keep the held K / V fragments in the accumulation registers
+#pragma unroll
+        for (int kb = 0; kb < C::KBD; ++kb) asm volatile("" : "+a"(fk[kb]), "+a"(vB[kb]));
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // B1: this pass's Q/dO/lse2/Dl (and K/V) are in LDS
+        __syncthreads();  // this pass's inputs have landed; the previous pass is done
+        if (rel_pending) {
+          release(rel, lane);  // its stores completed at the wait above
+          rel_pending = false;
+        }
+
+        // poll the previous slice's turn counter before the prefetch is
+        // issued, so that waiting for the poll does not wait for the prefetch
+        // (memory operations complete in issue order); without a turn to
+        // take, poll a word that is always zero
+        const bool need_turn = !atomic_dq && have_prev && prev.rank > 0;
+        const int* const poll_ptr = need_turn ? prev.cnt : p.ctrl + 3;
+        const int poll_expect = need_turn ? prev.rank : 0;
+        const int polled = __hip_atomic_load(poll_ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int acc_bytes = need_turn ? 4096 : 0;
 
         // prefetch the next pass into the other buffer (its readers finished
-        // before the previous pass's second barrier)
+        // before the barrier above)
         if (hp + 1 < NP) {
           LOAD_PASS(b, h, j, hp + 1, buf ^ 1);
         } else if (step + 1 < len) {
@@ -439,181 +745,84 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           LOAD_PASS(b, hk * G + tn.g, tn.j, 0, buf ^ 1);
         }
 
-#pragma unroll 1
-        for (int mt = 0; mt < C::QBP; ++mt) {
-          const int qb = hp * C::QBP + mt;  // 32-row block within the task
-          if (diag && w > qb) {
-            // keys of this wave all come after these queries: dS block is zero
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              *reinterpret_cast<bf16*>(lS + offW[r & 7] + (r >> 3) * 16 * C::RBS + 32 * mt * C::RBS) =
-                  (bf16)0.0f;
-            continue;
-          }
-          f32x16 sacc = {}, dpacc = {};
-          {
-            bf16x8 fq[2], fd[2], fk[2], fv[2];
-            fq[0] = lds_read16(lQ, offA[0] + 32 * mt * C::RBD);
-            fd[0] = lds_read16(lO, offA[0] + 32 * mt * C::RBD);
-            fk[0] = lds_read16(lK, offA[0] + 32 * w * C::RBD);
-            fv[0] = lds_read16(lV, offA[0] + 32 * w * C::RBD);
-#pragma unroll
-            for (int kb = 0; kb < C::KBD; ++kb) {
-              if (kb + 1 < C::KBD) {
-                const int n = (kb + 1) & 1;
-                fq[n] = lds_read16(lQ, offA[kb + 1] + 32 * mt * C::RBD);
-                fd[n] = lds_read16(lO, offA[kb + 1] + 32 * mt * C::RBD);
-                fk[n] = lds_read16(lK, offA[kb + 1] + 32 * w * C::RBD);
-                fv[n] = lds_read16(lV, offA[kb + 1] + 32 * w * C::RBD);
-              }
-              sacc = mfma(fq[kb & 1], fk[kb & 1], sacc);
-              dpacc = mfma(fd[kb & 1], fv[kb & 1], dpacc);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-          f32x4 l2[4], dl[4];
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            l2[k4] = *reinterpret_cast<const f32x4*>(lL + 4 * (32 * mt + 8 * k4 + 4 * hg));
-            dl[k4] = *reinterpret_cast<const f32x4*>(lDl + 4 * (32 * mt + 8 * k4 + 4 * hg));
-          }
-          bf16x8 pb[2], dsb[2];
-          if ((diag && qb == w) || kv_tail) {
-            // bit r of zb: element r is masked (key after query on the
-            // diagonal block, or key past the sequence end)
-            const unsigned zb = ((diag && qb == w) ? diag_bits : 0u) | ((kv_tail && !key_ok) ? 0xffffu : 0u);
-            softmax_block<true>(sacc, dpacc, l2, dl, p.scale_log2e, zb, pb, dsb);
-          } else {
-            softmax_block<false>(sacc, dpacc, l2, dl, p.scale_log2e, 0u, pb, dsb);
-          }
-          {
-            // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows of block mt
-            bf16x8 fa[2], fb[2];
-            fa[0] = lds_read_tr(lO, offT[0][0] + 32 * mt * C::RBD, offT[0][1] + 32 * mt * C::RBD);
-            fb[0] = lds_read_tr(lQ, offT[0][0] + 32 * mt * C::RBD, offT[0][1] + 32 * mt * C::RBD);
-#pragma unroll
-            for (int x = 0; x < 2 * C::DB; ++x) {
-              const int md = x >> 1, kq = x & 1;
-              if (x + 1 < 2 * C::DB) {
-                const int md1 = (x + 1) >> 1, kq1 = (x + 1) & 1;
-                const int base = (32 * mt + 16 * kq1) * C::RBD;
-                fa[(x + 1) & 1] = lds_read_tr(lO, offT[md1][0] + base, offT[md1][1] + base);
-                fb[(x + 1) & 1] = lds_read_tr(lQ, offT[md1][0] + base, offT[md1][1] + base);
-              }
-              dV[md] = mfma(fa[x & 1], pb[kq], dV[md]);
-              dK[md] = mfma(fb[x & 1], dsb[kq], dK[md]);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            *reinterpret_cast<bf16*>(lS + offW[r & 7] + (r >> 3) * 16 * C::RBS + 32 * mt * C::RBS) =
-                dsb[r >> 3][r & 7];
-        }
-        __syncthreads();  // B2: Q/dO/lse2/Dl reads of this pass done; dS complete
-
-        // dQ slice of this wave for this pass: rows hp*BQ + [32*MQ*qg, +32*MQ),
-        // features [32*db, +32)
-        const int tile = (b * p.Hq + h) * N + j;
-        const int slice = (tile * NP + hp) * C::NW + w;
-        float* const acc = p.dqacc + slice * (C::MQ * 1024);
-        int* const cnt = p.counters + slice;
-        const int rank = t.rank;
-        f32x16 dq[C::MQ];
-#pragma unroll
-        for (int m = 0; m < C::MQ; ++m) dq[m] = f32x16{};
+        // this pass's slice
+        Slice cur;
         {
-          bf16x8 fa[2][C::MQ], fb[2];
-          const int qrow0 = 32 * qg * C::MQ * C::RBS;
-#pragma unroll
-          for (int m = 0; m < C::MQ; ++m) fa[0][m] = lds_read16(lS, offS[0] + qrow0 + 32 * m * C::RBS);
-          fb[0] = lds_read_tr(lK, offK[0], offK[1]);
-#pragma unroll
-          for (int kb = 0; kb < C::KBT; ++kb) {
-            if (kb + 1 < C::KBT) {
-#pragma unroll
-              for (int m = 0; m < C::MQ; ++m)
-                fa[(kb + 1) & 1][m] = lds_read16(lS, offS[kb + 1] + qrow0 + 32 * m * C::RBS);
-              fb[(kb + 1) & 1] = lds_read_tr(lK, offK[0] + 16 * (kb + 1) * C::RBD,
-                                             offK[1] + 16 * (kb + 1) * C::RBD);
-            }
-#pragma unroll
-            for (int m = 0; m < C::MQ; ++m) dq[m] = mfma(fa[kb & 1][m], fb[kb & 1], dq[m]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          const int slice = (tile * NP + hp) * C::NW + w;
+          cur.acc = p.dqacc + slice * 1024;
+          cur.cnt = p.counters + slice;
+          cur.rank = t.rank;
+          cur.last = t.rank == ncontrib - 1;
+          const int r0 = j * T + hp * BQ + 32 * qg;
+          cur.dq_off = (b * S + r0) * rsq + h * D + 32 * db + c;
+          cur.rows_left = S - 1 - r0;
         }
 
-        if constexpr (atomic_dq) {
-          // element r of row block m of lane l at (m*16 + r)*64 + l: each
-          // atomic instruction covers 64 consecutive floats
+        unsigned zb[QBP];
 #pragma unroll
-          for (int m = 0; m < C::MQ; ++m)
+        for (int m = 0; m < QBP; ++m) {
+          const int qb = hp * QBP + m;  // 32-row block within the task
+          unsigned z = 0;
+          if (CAUSAL && i == j) z = w > qb ? 0xffffu : (w == qb ? diag_bits : 0u);
+          if (kv_tail && !key_ok) z = 0xffffu;
+          zb[m] = z;
+        }
+        pass_body<D, T, CAUSAL, atomic_dq>(lQ, lO, lL, lK, lS_cur, lS_prev, o, qg, hg, lane, p.scale_log2e,
+                                           masked, zb, fk, vB, dK, dV, fin, have_fin, dq_fin, old_fin, prev,
+                                           poll_ptr, poll_expect, polled, acc_bytes, p, rsq, gdq);
+        if (have_fin && !atomic_dq) {
+          rel = fin;
+          rel_pending = true;
+        }
+        fin = prev;
+        have_fin = have_prev;
+
+        if (hp == NP - 1 && t.seg_end) {
+          // last pass of this KV tile's run: finish this pass's dQ now, while
+          // the tile's fragments are still held
+          __syncthreads();  // every wave's dS of this pass is in LDS
+          // the slice of the previous pass is complete in registers: store it,
+          // and publish it and the slice stored during this pass before
+          // waiting for another turn (every chain of a lockstep group reaches
+          // this point at once, so holding them here would close a cycle)
+          if (have_fin) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              unsafeAtomicAdd(acc + (m * 16 + r) * 64 + lane, dq[m][r]);
-        } else {
-          const __amdgpu_buffer_rsrc_t racc =
-              __builtin_amdgcn_make_buffer_rsrc(acc, 0, C::MQ * 4096, 0x00020000);
-          const bool last = rank == contributors(mask, N, j) - 1;
-          if (rank > 0) {
-            wait_turn(cnt, rank, p.ctrl, p.spin_ticks, lane);
-            f32x4 old[C::MQ][4];
+            for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-            for (int m = 0; m < C::MQ; ++m)
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4)
-                old[m][q4] = __builtin_amdgcn_raw_buffer_load_b128(
-                    racc, (m * 4 * 64 + lane) * 16 + q4 * 1024, 0, kSC1);
-#pragma unroll
-            for (int m = 0; m < C::MQ; ++m)
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dq[m][4 * q4 + e] = old[m][q4][e] + dq[m][4 * q4 + e];
+              for (int e = 0; e < 4; ++e) dq_fin[4 * q4 + e] = old_fin[q4][e] + dq_fin[4 * q4 + e];
+            acc_finish<atomic_dq>(fin, dq_fin, lane, hg, rsq, p.scale, gdq);
           }
-          if (!last) {
-#pragma unroll
-            for (int m = 0; m < C::MQ; ++m) {
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 x = {dq[m][4 * q4], dq[m][4 * q4 + 1], dq[m][4 * q4 + 2], dq[m][4 * q4 + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(x, racc, (m * 4 * 64 + lane) * 16 + q4 * 1024, 0, kSC1);
-              }
-            }
-          } else {
-            // final value: dQ = scale * sum, bf16
-            bf16* const gdq = (bf16*)p.dq;
-            const int rs = p.Hq * D;
-            const int r0 = j * T + hp * BQ;
-            const int base = (b * S + r0) * rs + h * D + 32 * db + c;
-            const int last_row = S - 1 - r0;
-            if (r0 + BQ <= S) {
-#pragma unroll
-              for (int m = 0; m < C::MQ; ++m)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  const int ql = 32 * (qg * C::MQ + m) + 8 * (r >> 2) + 4 * hg + (r & 3);
-                  gdq[base + ql * rs] = (bf16)(dq[m][r] * p.scale);
-                }
-            } else {
-              // partial last tile: rows past S are not written
-#pragma unroll
-              for (int m = 0; m < C::MQ; ++m)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  const int ql = 32 * (qg * C::MQ + m) + 8 * (r >> 2) + 4 * hg + (r & 3);
-                  const int qc = min(ql, max(last_row, 0));
-                  const bf16 v = (bf16)(dq[m][r] * p.scale);
-                  if (ql <= last_row) gdq[base + qc * rs] = v;
-                }
-            }
+          order_point();
+          __builtin_amdgcn_s_waitcnt(0);
+          order_point();
+          if (!atomic_dq) {
+            if (rel_pending) release(rel, lane);
+            if (have_fin) release(fin, lane);
           }
+          f32x16 dq = dq_products<D, T, CAUSAL>(lS_cur, lK, o, qg);
+          const bool ct = !atomic_dq && cur.rank > 0;
+          if (ct) {
+            const int pv = __hip_atomic_load(cur.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            acquire(cur.cnt, cur.rank, pv, p.ctrl, p.spin_ticks, lane);
+          }
+          f32x4 old[4];
+          acc_load(cur.acc, ct ? 4096 : 0, lane, old);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dq[4 * q4 + e] = old[q4][e] + dq[4 * q4 + e];
+          acc_finish<atomic_dq>(cur, dq, lane, hg, rsq, p.scale, gdq);
           // release: all of this wave's accumulator stores acknowledged first
           order_point();
           __builtin_amdgcn_s_waitcnt(0);
           order_point();
-          if (lane == 0)
-            __hip_atomic_store(cnt, rank + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (!atomic_dq) release(cur, lane);
+          rel_pending = false;
+          have_fin = false;
+          have_prev = false;
+        } else {
+          prev = cur;
+          have_prev = true;
         }
       }
 
@@ -647,20 +856,18 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // Atomic reference only: dQ partial sums -> bf16 dq.  One thread per float of
-// the accumulator, laid out as [tile][pass][wave slice][row block m][r][lane].
+// the accumulator, laid out as [tile][pass][wave slice][r][lane].
 template <int D, int T>
 __global__ __launch_bounds__(256) void bwd_finalize(FinParams p) {
   using C = BwdCfg<D, T, false>;
-  constexpr int NW = C::NW, DB = C::DB, MQ = C::MQ, NP = C::NP;
+  constexpr int NW = C::NW, DB = C::DB, NP = C::NP;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)p.B * p.Hq * p.N * NP * NW * MQ * 16 * 64;
+  const long long total = (long long)p.B * p.Hq * p.N * NP * NW * 16 * 64;
   if (idx >= total) return;
   const int lane = (int)(idx % 64);
   long long rest = idx / 64;
   const int r = (int)(rest % 16);
   rest /= 16;
-  const int m = (int)(rest % MQ);
-  rest /= MQ;
   const int w = (int)(rest % NW);
   rest /= NW;
   const int hp = (int)(rest % NP);
@@ -669,7 +876,7 @@ __global__ __launch_bounds__(256) void bwd_finalize(FinParams p) {
   const long long bh = rest / p.N;
   const int b = (int)(bh / p.Hq), h = (int)(bh % p.Hq);
   const int qg = w / DB, db = w % DB;
-  const int ql = hp * C::BQ + 32 * (qg * MQ + m) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  const int ql = hp * C::BQ + 32 * qg + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
   const int row = j * T + ql;
   if (row < p.S)
     ((bf16*)p.dq)[((size_t)((size_t)b * p.S + row) * p.Hq + h) * D + 32 * db + (lane & 31)] =

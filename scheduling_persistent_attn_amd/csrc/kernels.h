@@ -10,14 +10,15 @@ struct PreParams {
   const void* o;
   const void* dout;
   const float* lse;
-  float* delta;      // [B*Hq][NT]
-  float* lse2;       // [B*Hq][NT]
+  float* delta;      // [B*Hq][NT]: -rowsum(dO * O), 0 past S
+  float* lse2;       // [B*Hq][NT]: -lse / scale, -inf past S
   int* counters;     // n_counters ints, zeroed
   int* ctrl;         // 64 ints, zeroed
   float* dqacc;      // zeroed when zero_dqacc (atomic schedule)
   long long n_counters;
   long long n_dqacc;
   int zero_dqacc;
+  float inv_scale;   // 1 / softmax scale
   int B, Hq, S, D, NT;
 };
 
@@ -29,8 +30,8 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  const float* delta;
-  const float* lse2;
+  const float* delta;  // -Dl per padded query row
+  const float* lse2;   // -lse / scale per padded query row
   float* dqacc;
   int* counters;
   int* ctrl;

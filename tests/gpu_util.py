@@ -60,7 +60,7 @@ def contributors(causal, N, j):
 def expected_counters(B, Hq, S, D, causal):
     T = dash.dash_attn_tile_size(S, D)
     N = (S + T - 1) // T
-    NW = T * T // 2048
+    NW = T * D // 1024  # one counter per 32x32 slice of a dQ tile
     want = np.zeros((B, Hq, N, NW), dtype=np.int64)
     for j in range(N):
         want[:, :, j, :] = contributors(causal, N, j)
@@ -70,7 +70,7 @@ def expected_counters(B, Hq, S, D, causal):
 def read_counters(workspace, B, Hq, S, D):
     T = dash.dash_attn_tile_size(S, D)
     N = (S + T - 1) // T
-    NW = T * T // 2048
+    NW = T * D // 1024  # one counter per 32x32 slice of a dQ tile
     n = B * Hq * N * NW
     ws = workspace.view(torch.int32)
     return ws[64:64 + n].cpu().numpy().reshape(B, Hq, N, NW)
