@@ -29,6 +29,12 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 
+# per-source additions: the backward kernel keeps its matrix-product
+# accumulators in the vector registers (the softmax reads S and dP and the
+# dQ partial sum is loaded straight into its accumulator), and pins the
+# operands it holds for a whole KV tile to the accumulation registers itself
+EXTRA = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -47,7 +53,7 @@ def build(verbose=False):
         if src in HOST_ONLY:
             cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-c", os.path.join(CSRC, src), "-o", obj]
         else:
-            cmd = [cc] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("compile failed: %s\n%s%s" % (" ".join(cmd), res.stdout, res.stderr))

@@ -185,6 +185,16 @@ constexpr int kSC1 = 16;  // cache-policy operand of the buffer intrinsics: sc1
 
 __device__ __forceinline__ void order_point() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
+// s_waitcnt for the vector-memory counter only: at most n of this wave's
+// vector memory operations outstanding.  They complete in issue order, so
+// this waits for everything but the last n issued.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
 // Turn wait with a watchdog.  Executed by a whole wave; lane 0 polls.  Returns
 // false (and raises the workspace error flag) on timeout or if another wave
 // already raised it.
@@ -241,12 +251,50 @@ __device__ __forceinline__ void load_tile_async(const bf16* g, int rs, int nvali
   }
 }
 
-// Asynchronous copy of N (32 or 64) consecutive floats (a row range of the
-// padded -lse/scale or -Dl arrays) into LDS: one dword load, lane l -> float l.
-template <int N>
-__device__ __forceinline__ void load_row_vec_async(const float* src, const char* dst, int lane) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, 4 * N, 0x00020000);
-  if (N == 64 || lane < N) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
+// ---------------------------------------------------------------------------
+// Buffer descriptors of one task's per-pass inputs: the Q and dO rows of its
+// query tile (range-limited to rows < S, which read as zero) and the tile's
+// -lse/scale and -Dl values.  A pass's rows are a scalar offset from these.
+struct TaskSrc {
+  __amdgpu_buffer_rsrc_t q, o, l, dl;
+};
+
+__device__ __forceinline__ TaskSrc task_src(const BwdParams& p, int D, int T, int b, int h, int j) {
+  const int rs = p.Hq * D;
+  const int r0 = j * T;
+  const int off = ((b * p.S + r0) * p.Hq + h) * D;
+  const int nv = p.S - r0;
+  const int nbytes = nv <= 0 ? 0 : ((nv - 1) * rs + D) * 2;
+  const int lrow = ((b * p.Hq + h) * p.N + j) * T;
+  TaskSrc t;
+  t.q = __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)p.q + off), 0, nbytes, 0x00020000);
+  t.o = __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)p.dout + off), 0, nbytes, 0x00020000);
+  t.l = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse2 + lrow), 0, 4 * T, 0x00020000);
+  t.dl = __builtin_amdgcn_make_buffer_rsrc((void*)(p.delta + lrow), 0, 4 * T, 0x00020000);
+  return t;
+}
+
+// Asynchronous copy of pass hp of a task (BQ rows of Q and dO, and their
+// -lse/scale, -Dl) into LDS buffers, as 1 KB direct-to-LDS blocks; wave w
+// issues blocks w, w + NW, ... (the slot pattern of load_tile_async).  voff
+// is the lane's byte offset within a block, (row0 * rs + chunk0 * 8) * 2.
+template <int D, int BQ, int NW>
+__device__ __forceinline__ void load_pass_async(const TaskSrc& ts, int hp, int rs, int voff, char* dq_dst,
+                                                char* do_dst, char* l_dst, int w, int lane) {
+  constexpr int BLK = BQ * 2 * D / 1024;
+  constexpr int RPS = 2 * D == 256 ? 1 : 2;  // rows per 256-byte super-row
+  static_assert(BLK % NW == 0, "whole blocks per wave");
+  const int soff0 = hp * BQ * rs * 2;
+#pragma unroll
+  for (int k = 0; k < BLK / NW; ++k) {
+    const int blk = w + k * NW;
+    const int soff = soff0 + k * 4 * NW * RPS * rs * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.q, (lds_void*)(dq_dst + blk * 1024), 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.o, (lds_void*)(do_dst + blk * 1024), 16, voff, soff, 0, 0);
+  }
+  if (w < 2 && (BQ == 64 || lane < BQ))
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? ts.l : ts.dl, (lds_void*)(l_dst + w * 4 * BQ), 4,
+                                             lane * 4, hp * BQ * 4, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -282,8 +330,8 @@ struct BwdCfg {
   static constexpr int OFF_K = 0;
   static constexpr int OFF_Q = K_TILE;                 // + buf * Q_TILE
   static constexpr int OFF_DO = OFF_Q + 2 * Q_TILE;    // + buf * Q_TILE
-  static constexpr int OFF_DS = OFF_DO + 2 * Q_TILE;   // + buf * S_TILE
-  static constexpr int OFF_LD = OFF_DS + 2 * S_TILE;   // [buf][-lse/scale | -Dl][BQ] fp32
+  static constexpr int OFF_DS = OFF_DO + 2 * Q_TILE;   // + buf * S_TILE, 3 buffers
+  static constexpr int OFF_LD = OFF_DS + 3 * S_TILE;   // [buf][-lse/scale | -Dl][BQ] fp32
   static constexpr int OFF_MISC = OFF_LD + 2 * 2 * 4 * BQ;
   static constexpr int LDS_BYTES = OFF_MISC + 16;
   static_assert(T >= D && NW % DB == 0 && T % BQ == 0, "tile shape");
@@ -347,25 +395,22 @@ __device__ __forceinline__ void softmax_block(const f32x16& sacc, const f32x16& 
 }
 
 // This wave's dQ slice for one pass: 32 rows (block qg) x 32 features (block
-// db), A = dS rows (LDS), B = K^T (transposing reads of the resident K tile).
+// db), A = dS rows (LDS), B = K^T fragments (registers), accumulated onto c
+// (the loaded partial sum of the earlier contributors, or zero).
 template <int D, int T, bool CAUSAL>
-__device__ __forceinline__ f32x16 dq_products(const char* lS, const char* lK, const LaneOffs<D, T>& o,
-                                              int qg) {
+__device__ __forceinline__ f32x16 dq_products(const char* lS, const LaneOffs<D, T>& o, int qg,
+                                              const bf16x8* fkt, f32x16 c) {
   using C = BwdCfg<D, T, CAUSAL>;
-  f32x16 dq = {};
   const int row0 = 32 * qg * C::RBS;
-  bf16x8 fa[2], fb[2];
+  bf16x8 fa[3];
   fa[0] = lds_read16(lS, o.S(0) + row0);
-  fb[0] = lds_read_tr(lK, o.kt[0], o.kt[1]);
+  fa[1] = lds_read16(lS, o.S(1) + row0);
 #pragma unroll
   for (int kb = 0; kb < C::KBT; ++kb) {
-    if (kb + 1 < C::KBT) {
-      fa[(kb + 1) & 1] = lds_read16(lS, o.S(kb + 1) + row0);
-      fb[(kb + 1) & 1] = lds_read_tr(lK, o.kt[0] + 16 * (kb + 1) * C::RBD, o.kt[1] + 16 * (kb + 1) * C::RBD);
-    }
-    dq = mfma(fa[kb & 1], fb[kb & 1], dq);
+    if (kb + 2 < C::KBT) fa[(kb + 2) % 3] = lds_read16(lS, o.S(kb + 2) + row0);
+    c = mfma(fa[kb % 3], fkt[kb], c);
   }
-  return dq;
+  return c;
 }
 
 // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows of block m of the
@@ -395,10 +440,16 @@ __device__ __forceinline__ void dvdk_block(const char* lQ, const char* lO, const
 // float (r / 4) * 256 + 4 * l + r % 4, i.e. four fully coalesced 1 KB rows.
 // With nbytes = 0 every load is out of range and returns zeros (used when
 // there is no partial sum to add).
-__device__ __forceinline__ void acc_load(float* acc, int nbytes, int lane, f32x4* old) {
+__device__ __forceinline__ f32x16 acc_load(float* acc, int nbytes, int lane) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(acc, 0, nbytes, 0x00020000);
+  f32x16 v;
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) old[q4] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + q4 * 1024, 0, kSC1);
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + q4 * 1024, 0, kSC1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * q4 + e] = x[e];
+  }
+  return v;
 }
 
 // Second half of a slice's reduction: dq + old (the loaded partial sum, zero
@@ -458,30 +509,27 @@ __device__ __forceinline__ void acquire(const int* cnt, int expect, int polled, 
 
 // One pass of the current task, plus two stages of the ordered reductions of
 // earlier passes:
-//   * slice `fin` (two passes back), whose dQ partial dq_fin and loaded
-//     partial sum old_fin the previous pass left in registers: added and
-//     stored (or, for the last contributor, written to dq) after the S/dP
-//     products, when fin_on;
+//   * slice `ld` (two passes back): its dQ product is formed from lS_ld on
+//     top of the partial sum the previous pass loaded into dq_ld, then stored
+//     (or, for the last contributor, written to dq) -- when ld_on;
 //   * slice `prev` (the previous pass): its turn, polled at the start of the
-//     pass, is checked after the S/dP products, then its accumulator loads are
-//     issued (zeros when there is no partial sum to add) and its dQ product
-//     is formed from lS_prev; both are returned in dq_fin / old_fin for the
-//     next pass.  (Without a previous pass the product is formed and
-//     dropped.)
+//     pass, is checked at the end, then its partial sum is loaded into dq_ld
+//     for the next pass (zeros when there is nothing to add).
 // The loads thus have a whole pass to arrive, and the stores a whole pass to
-// complete before the counter is bumped after the next barrier.  The code
-// from the acquire to the end has no branches, so that the compiler can
-// interleave the softmax with the dQ and dV/dK products.  Writes dS of this
-// pass into lS_cur.  When masked, elements with their bit set in zb[m] start
-// at -inf (P = 0).
+// complete before the counter is bumped after the next barrier.  Everything
+// from the first product to the last dS write has no branches, so that the
+// compiler can interleave the softmax with the dQ and dV/dK products (without
+// a slice two passes back the dQ product is formed and dropped).  Writes dS
+// of this pass into lS_cur.  When masked, elements with their bit set in zb[m]
+// start at -inf (P = 0).
 template <int D, int T, bool CAUSAL, bool ATOMIC>
-__device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const char* lL, const char* lK,
-                                          char* lS_cur, const char* lS_prev, const LaneOffs<D, T>& o, int qg,
-                                          int hg, int lane, float scale_log2e, bool masked, const unsigned* zb,
-                                          const bf16x8* fk, const bf16x8* vB, f32x16* dK, f32x16* dV,
-                                          const Slice& fin, bool fin_on, f32x16& dq_fin, f32x4* old_fin,
-                                          const Slice& prev, const int* poll_ptr, int poll_expect, int polled,
-                                          int acc_bytes, const BwdParams& p, int rs, bf16* gdq) {
+__device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const char* lL, char* lS_cur,
+                                          const char* lS_ld, const LaneOffs<D, T>& o, int qg, int hg, int lane,
+                                          float scale_log2e, bool masked, const unsigned* zb, const bf16x8* fk,
+                                          const bf16x8* vB, const bf16x8* fkt, f32x16* dK, f32x16* dV,
+                                          const Slice& ld, bool ld_on, f32x16& dq_ld, const Slice& prev,
+                                          const int* poll_ptr, int poll_expect, int polled, int acc_bytes,
+                                          const BwdParams& p, int rs, bf16* gdq) {
   using C = BwdCfg<D, T, CAUSAL>;
   constexpr int QBP = C::QBP;
   // ---- S and dP of the pass's 32-row blocks; the accumulators start at
@@ -506,49 +554,37 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
       for (int r = 0; r < 16; ++r) sa[m][r] = ((zb[m] >> r) & 1u) ? -__builtin_inff() : sa[m][r];
   }
   {
-    bf16x8 fq[2][QBP], fd[2][QBP];
+    // fragments two k-blocks ahead of the products that use them
+    bf16x8 fq[3][QBP], fd[3][QBP];
 #pragma unroll
-    for (int m = 0; m < QBP; ++m) {
-      fq[0][m] = lds_read16(lQ, o.A(0) + 32 * m * C::RBD);
-      fd[0][m] = lds_read16(lO, o.A(0) + 32 * m * C::RBD);
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int m = 0; m < QBP; ++m) {
+        fq[kb][m] = lds_read16(lQ, o.A(kb) + 32 * m * C::RBD);
+        fd[kb][m] = lds_read16(lO, o.A(kb) + 32 * m * C::RBD);
+      }
 #pragma unroll
     for (int kb = 0; kb < C::KBD; ++kb) {
-      const int n = (kb + 1) & 1;
-      if (kb + 1 < C::KBD) {
+      if (kb + 2 < C::KBD) {
 #pragma unroll
         for (int m = 0; m < QBP; ++m) {
-          fq[n][m] = lds_read16(lQ, o.A(kb + 1) + 32 * m * C::RBD);
-          fd[n][m] = lds_read16(lO, o.A(kb + 1) + 32 * m * C::RBD);
+          fq[(kb + 2) % 3][m] = lds_read16(lQ, o.A(kb + 2) + 32 * m * C::RBD);
+          fd[(kb + 2) % 3][m] = lds_read16(lO, o.A(kb + 2) + 32 * m * C::RBD);
         }
       }
 #pragma unroll
       for (int m = 0; m < QBP; ++m) {
-        sa[m] = mfma(fq[kb & 1][m], fk[kb], sa[m]);
-        pa[m] = mfma(fd[kb & 1][m], vB[kb], pa[m]);
+        sa[m] = mfma(fq[kb % 3][m], fk[kb], sa[m]);
+        pa[m] = mfma(fd[kb % 3][m], vB[kb], pa[m]);
       }
     }
   }
 
-  // ---- the slice of two passes back: add and store
-  if (fin_on) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dq_fin[4 * q4 + e] = old_fin[q4][e] + dq_fin[4 * q4 + e];
-    acc_finish<ATOMIC>(fin, dq_fin, lane, hg, rs, p.scale, gdq);
-  }
-
-  // ---- turn of the previous slice, then its accumulator loads (zeros when
-  // there is nothing to add)
-  if constexpr (!ATOMIC) acquire(poll_ptr, poll_expect, polled, p.ctrl, p.spin_ticks, lane);
-  acc_load(prev.acc, acc_bytes, lane, old_fin);
-
-  // ---- softmax next to the dQ product of the previous pass
+  // ---- dQ of the slice two passes back, next to the softmax
+  const f32x16 dq = dq_products<D, T, CAUSAL>(lS_ld, o, qg, fkt, dq_ld);
   bf16x8 pb[QBP][2], dsb[QBP][2];
 #pragma unroll
   for (int m = 0; m < QBP; ++m) softmax_block(sa[m], pa[m], scale_log2e, pb[m], dsb[m]);
-  dq_fin = dq_products<D, T, CAUSAL>(lS_prev, lK, o, qg);
 
   // ---- dV^T += dO^T P, dK^T += Q^T dS; dS -> LDS
 #pragma unroll
@@ -559,6 +595,18 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
       *reinterpret_cast<bf16*>(lS_cur + o.W(r & 7) + (r >> 3) * 16 * C::RBS + 32 * m * C::RBS) =
           dsb[m][r >> 3][r & 7];
   }
+
+  // ---- store the slice two passes back
+  if (ld_on) acc_finish<ATOMIC>(ld, dq, lane, hg, rs, p.scale, gdq);
+
+  // ---- turn of the previous slice, then its partial sum: these four loads
+  // are the last vector memory operations of the pass (the next pass's
+  // barrier waits for everything before them)
+  order_point();
+  if constexpr (!ATOMIC) acquire(poll_ptr, poll_expect, polled, p.ctrl, p.spin_ticks, lane);
+  order_point();
+  dq_ld = acc_load(prev.acc, acc_bytes, lane);
+  order_point();
 }
 
 template <int D, int T, bool CAUSAL, int SCHED>
@@ -610,34 +658,27 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   slot_source<C::RBD>(4 * w + (lane >> 4), lane & 15, &ldRow0, &ldChunk0);
 
   f32x16 dK[C::DB], dV[C::DB];
-  // operands from the current KV tile, held for its whole run (dQ reads K^T
-  // from the resident K tile):
+  // operands from the current KV tile, held for its whole run:
   bf16x8 fk[C::KBD];   // K rows 32w + c (B operand of S)
   bf16x8 vB[C::KBD];   // V rows 32w + c (B operand of dP)
+  bf16x8 fkt[C::KBT];  // K^T, features of block db (B operand of dQ)
 
-  // Q, dO, -lse/scale, -Dl of rows [j*T + hp*BQ, +BQ) of head h into buffer buf
-#define LOAD_PASS(b_, h_, j_, hp_, buf_)                                                     \
-  do {                                                                                       \
-    const int r0_ = (j_) * T + (hp_) * BQ;                                                   \
-    const int off_ = (((b_) * S + r0_) * p.Hq + (h_)) * D;                                   \
-    load_tile_async<D, BQ, C::NW>((const bf16*)p.q + off_, rsq, S - r0_,                     \
-                                  smem + C::OFF_Q + (buf_) * C::Q_TILE, w, ldRow0, ldChunk0); \
-    load_tile_async<D, BQ, C::NW>((const bf16*)p.dout + off_, rsq, S - r0_,                  \
-                                  smem + C::OFF_DO + (buf_) * C::Q_TILE, w, ldRow0, ldChunk0); \
-    const int row0_ = (((b_) * p.Hq + (h_)) * N + (j_)) * T + (hp_) * BQ;                    \
-    if (w < 2)                                                                               \
-      load_row_vec_async<BQ>((w == 0 ? p.lse2 : p.delta) + row0_,                            \
-                             smem + C::OFF_LD + ((buf_) * 2 + w) * 4 * BQ, lane);            \
-  } while (0)
+  // lane's byte offset of its 16-byte slot within a block of Q / dO rows
+  const int voffQ = (ldRow0 * rsq + ldChunk0 * 8) * 2;
+#define LOAD_PASS(ts_, hp_, buf_)                                                              \
+  load_pass_async<D, BQ, C::NW>((ts_), (hp_), rsq, voffQ, smem + C::OFF_Q + (buf_) * C::Q_TILE, \
+                                smem + C::OFF_DO + (buf_) * C::Q_TILE,                        \
+                                smem + C::OFF_LD + (buf_) * 2 * 4 * BQ, w, lane)
 
   int gp = 0;        // passes processed by this workgroup (selects the buffers)
-  // reduction pipeline: prev = slice of the previous pass (dS in LDS), fin =
-  // slice whose dQ partial and loaded partial sum are in dq_fin / old_fin,
-  // rel = slice whose stores are issued but whose counter is not yet bumped
-  Slice prev = {}, fin = {}, rel = {};
-  bool have_prev = false, have_fin = false, rel_pending = false;
-  f32x16 dq_fin = {};
-  f32x4 old_fin[4] = {};
+  // reduction pipeline: prev = slice of the previous pass (dS in LDS), ld =
+  // slice of two passes back (dS in LDS, partial sum loaded into dq_ld), rel
+  // = slice whose stores are issued but whose counter is not yet bumped
+  Slice prev = {}, ld = {}, rel = {};
+  bool have_prev = false, have_ld = false, rel_pending = false;
+  f32x16 dq_ld = {};
+  int sb = 0;  // dS buffer of the current pass (of three)
+  bool acc_tail = false;  // the last four vector memory operations are partial-sum loads
   for (;;) {
     __syncthreads();  // previous item's LDS use complete
     int* const misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
@@ -654,14 +695,19 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
     const int local = item - grp * p.items_per_group;
     const int b = grp / p.Hkv, hk = grp - b * p.Hkv;
     const int len = item_len(mask, SCHED, N, G, local);
-    {
-      const Task t0 = task_at(mask, SCHED, N, G, local, 0);
-      LOAD_PASS(b, hk * G + t0.g, t0.j, 0, gp & 1);
-    }
+    Task tn = task_at(mask, SCHED, N, G, local, 0);
+    TaskSrc tsn = task_src(p, D, T, b, hk * G + tn.g, tn.j);
+    LOAD_PASS(tsn, 0, gp & 1);
 
     for (int step = 0; step < len; ++step) {
-      const Task t = task_at(mask, SCHED, N, G, local, step);
+      const Task t = tn;
+      const TaskSrc ts = tsn;
       const int i = t.i, j = t.j, h = hk * G + t.g;
+      const bool has_next = step + 1 < len;
+      if (has_next) {
+        tn = task_at(mask, SCHED, N, G, local, step + 1);
+        tsn = task_src(p, D, T, b, hk * G + tn.g, tn.j);
+      }
       if (t.seg_begin) {
         // new KV tile: K through LDS into this wave's K and K^T fragments, V
         // rows straight into registers
@@ -686,11 +732,16 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         __syncthreads();  // the K tile is in LDS
 #pragma unroll
         for (int kb = 0; kb < C::KBD; ++kb) fk[kb] = lds_read16(lK, o.A(kb) + 32 * w * C::RBD);
+#pragma unroll
+        for (int kb = 0; kb < C::KBT; ++kb)
+          fkt[kb] = lds_read_tr(lK, o.kt[0] + 16 * kb * C::RBD, o.kt[1] + 16 * kb * C::RBD);
         // the held fragments live in the accumulation registers (MFMA takes
         // its B operand from there), leaving the vector registers to the
         // per-pass work
 #pragma unroll
         for (int kb = 0; kb < C::KBD; ++kb) asm volatile("" : "+a"(fk[kb]), "+a"(vB[kb]));
+#pragma unroll
+        for (int kb = 0; kb < C::KBT; ++kb) asm volatile("" : "+a"(fkt[kb]));
 #pragma unroll
         for (int md = 0; md < C::DB; ++md) {
           dK[md] = f32x16{};
@@ -701,16 +752,20 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
       const int key_local = 32 * w + c;
       const bool key_ok = i * T + key_local < S;
       const bool masked = (CAUSAL && i == j) || kv_tail;
-      const int tile = (b * p.Hq + h) * N + j;
-      const int ncontrib = contributors(mask, N, j);
+      // this task's slices: pass hp is slice (tile * NP + hp) * NW + w
+      const int slice0 = ((b * p.Hq + h) * N + j) * NP * C::NW + w;
+      const bool last = t.rank == contributors(mask, N, j) - 1;
+      const int r00 = j * T + 32 * qg;
+      const int dq_off0 = (b * S + r00) * rsq + h * D + 32 * db + c;
 
       for (int hp = 0; hp < NP; ++hp, ++gp) {
         const int buf = gp & 1;
         const char* const lQ = smem + C::OFF_Q + buf * C::Q_TILE;
         const char* const lO = smem + C::OFF_DO + buf * C::Q_TILE;
         const char* const lL = smem + C::OFF_LD + buf * 2 * 4 * BQ;
-        char* const lS_cur = smem + C::OFF_DS + buf * C::S_TILE;
-        const char* const lS_prev = smem + C::OFF_DS + (buf ^ 1) * C::S_TILE;
+        char* const lS_cur = smem + C::OFF_DS + sb * C::S_TILE;
+        const int sb_ld = sb == 0 ? 1 : (sb == 1 ? 2 : 0);  // two passes back
+        const char* const lS_ld = smem + C::OFF_DS + sb_ld * C::S_TILE;
         // re-materialise the offset bases each pass, so that the compiler
         // derives the per-access offsets here instead of keeping dozens of
         // them alive across the loop
@@ -719,8 +774,23 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         // and keep the held K / V fragments in the accumulation registers
 #pragma unroll
         for (int kb = 0; kb < C::KBD; ++kb) asm volatile("" : "+a"(fk[kb]), "+a"(vB[kb]));
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // this pass's inputs have landed; the previous pass is done
+#pragma unroll
+        for (int kb = 0; kb < C::KBT; ++kb) asm volatile("" : "+a"(fkt[kb]));
+        // this pass's inputs and the previous pass's accumulator stores have
+        // completed: everything but the partial-sum loads the previous pass
+        // issued last (when it ran a pass body), which the dQ product waits
+        // for itself
+        if (acc_tail)
+          wait_vm<4>();
+        else
+          __builtin_amdgcn_s_waitcnt(0);
+        // the previous pass's LDS writes (dS) are complete once lgkmcnt
+        // drains; no global memory is shared between the waves here, so the
+        // barrier needs no memory fence
+        order_point();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+        __builtin_amdgcn_s_barrier();
+        order_point();
         if (rel_pending) {
           release(rel, lane);  // its stores completed at the wait above
           rel_pending = false;
@@ -739,23 +809,21 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         // prefetch the next pass into the other buffer (its readers finished
         // before the barrier above)
         if (hp + 1 < NP) {
-          LOAD_PASS(b, h, j, hp + 1, buf ^ 1);
-        } else if (step + 1 < len) {
-          const Task tn = task_at(mask, SCHED, N, G, local, step + 1);
-          LOAD_PASS(b, hk * G + tn.g, tn.j, 0, buf ^ 1);
+          LOAD_PASS(ts, hp + 1, buf ^ 1);
+        } else if (has_next) {
+          LOAD_PASS(tsn, 0, buf ^ 1);
         }
 
         // this pass's slice
         Slice cur;
         {
-          const int slice = (tile * NP + hp) * C::NW + w;
+          const int slice = slice0 + hp * C::NW;
           cur.acc = p.dqacc + slice * 1024;
           cur.cnt = p.counters + slice;
           cur.rank = t.rank;
-          cur.last = t.rank == ncontrib - 1;
-          const int r0 = j * T + hp * BQ + 32 * qg;
-          cur.dq_off = (b * S + r0) * rsq + h * D + 32 * db + c;
-          cur.rows_left = S - 1 - r0;
+          cur.last = last;
+          cur.dq_off = dq_off0 + hp * BQ * rsq;
+          cur.rows_left = S - 1 - r00 - hp * BQ;
         }
 
         unsigned zb[QBP];
@@ -767,50 +835,44 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           if (kv_tail && !key_ok) z = 0xffffu;
           zb[m] = z;
         }
-        pass_body<D, T, CAUSAL, atomic_dq>(lQ, lO, lL, lK, lS_cur, lS_prev, o, qg, hg, lane, p.scale_log2e,
-                                           masked, zb, fk, vB, dK, dV, fin, have_fin, dq_fin, old_fin, prev,
-                                           poll_ptr, poll_expect, polled, acc_bytes, p, rsq, gdq);
-        if (have_fin && !atomic_dq) {
-          rel = fin;
+        pass_body<D, T, CAUSAL, atomic_dq>(lQ, lO, lL, lS_cur, lS_ld, o, qg, hg, lane, p.scale_log2e, masked, zb,
+                                           fk, vB, fkt, dK, dV, ld, have_ld, dq_ld, prev, poll_ptr, poll_expect,
+                                           polled, acc_bytes, p, rsq, gdq);
+        acc_tail = true;
+        if (have_ld && !atomic_dq) {
+          rel = ld;
           rel_pending = true;
         }
-        fin = prev;
-        have_fin = have_prev;
+        ld = prev;
+        have_ld = have_prev;
 
         if (hp == NP - 1 && t.seg_end) {
-          // last pass of this KV tile's run: finish this pass's dQ now, while
-          // the tile's fragments are still held
+          // last pass of this KV tile's run: finish the two open slices now,
+          // while the tile's fragments are still held
           __syncthreads();  // every wave's dS of this pass is in LDS
-          // the slice of the previous pass is complete in registers: store it,
+          // the previous pass's slice (partial sum already loaded): store it,
           // and publish it and the slice stored during this pass before
           // waiting for another turn (every chain of a lockstep group reaches
           // this point at once, so holding them here would close a cycle)
-          if (have_fin) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) dq_fin[4 * q4 + e] = old_fin[q4][e] + dq_fin[4 * q4 + e];
-            acc_finish<atomic_dq>(fin, dq_fin, lane, hg, rsq, p.scale, gdq);
+          const int sb_prev = sb == 0 ? 2 : sb - 1;
+          if (have_ld) {
+            const f32x16 dq = dq_products<D, T, CAUSAL>(smem + C::OFF_DS + sb_prev * C::S_TILE, o, qg, fkt, dq_ld);
+            acc_finish<atomic_dq>(ld, dq, lane, hg, rsq, p.scale, gdq);
           }
           order_point();
           __builtin_amdgcn_s_waitcnt(0);
           order_point();
           if (!atomic_dq) {
             if (rel_pending) release(rel, lane);
-            if (have_fin) release(fin, lane);
+            if (have_ld) release(ld, lane);
           }
-          f32x16 dq = dq_products<D, T, CAUSAL>(lS_cur, lK, o, qg);
           const bool ct = !atomic_dq && cur.rank > 0;
           if (ct) {
             const int pv = __hip_atomic_load(cur.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             acquire(cur.cnt, cur.rank, pv, p.ctrl, p.spin_ticks, lane);
           }
-          f32x4 old[4];
-          acc_load(cur.acc, ct ? 4096 : 0, lane, old);
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dq[4 * q4 + e] = old[q4][e] + dq[4 * q4 + e];
+          const f32x16 dq =
+              dq_products<D, T, CAUSAL>(lS_cur, o, qg, fkt, acc_load(cur.acc, ct ? 4096 : 0, lane));
           acc_finish<atomic_dq>(cur, dq, lane, hg, rsq, p.scale, gdq);
           // release: all of this wave's accumulator stores acknowledged first
           order_point();
@@ -818,12 +880,14 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           order_point();
           if (!atomic_dq) release(cur, lane);
           rel_pending = false;
-          have_fin = false;
+          have_ld = false;
           have_prev = false;
+          acc_tail = false;
         } else {
           prev = cur;
           have_prev = true;
         }
+        sb = sb == 2 ? 0 : sb + 1;
       }
 
       if (t.seg_end) {
