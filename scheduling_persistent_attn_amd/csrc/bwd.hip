@@ -252,49 +252,57 @@ __device__ __forceinline__ void load_tile_async(const bf16* g, int rs, int nvali
 }
 
 // ---------------------------------------------------------------------------
-// Buffer descriptors of one task's per-pass inputs: the Q and dO rows of its
-// query tile (range-limited to rows < S, which read as zero) and the tile's
-// -lse/scale and -Dl values.  A pass's rows are a scalar offset from these.
-struct TaskSrc {
-  __amdgpu_buffer_rsrc_t q, o, l, dl;
+// The inputs of one pass staged in registers on their way to LDS: this
+// lane's 16-byte slots of the BQ rows of Q and dO (the slots the direct-to-LDS
+// copies of load_tile_async fill) and one -lse/scale (wave 0) or -Dl (wave 1)
+// value.  Loading into registers and writing LDS at the end of the pass keeps
+// the LDS buffers out of the memory counter, so reads of the current buffer
+// never wait for the next pass's copy.  Every wave issues the same 2 KQ + 1
+// loads in every pass (out of range, returning zeros, when there is no next
+// pass), which keeps the compiler's counter waits for older loads exact.
+template <int D, int BQ, int NW>
+struct PassStage {
+  static constexpr int KQ = BQ * 2 * D / 1024 / NW;  // 1 KB blocks per wave and tensor
+  f32x4 q[KQ], o[KQ];
+  unsigned l;  // bit pattern of the fp32 value
 };
 
-__device__ __forceinline__ TaskSrc task_src(const BwdParams& p, int D, int T, int b, int h, int j) {
+template <int D, int BQ, int NW>
+__device__ __forceinline__ void stage_load(PassStage<D, BQ, NW>& st, const BwdParams& p, int T, int b, int h,
+                                           int j, int hp, bool valid, int voff, int w, int lane) {
+  constexpr int RPS = 2 * D == 256 ? 1 : 2;  // rows per 256-byte super-row
+  static_assert((BQ * 2 * D / 1024) % NW == 0, "whole blocks per wave");
   const int rs = p.Hq * D;
-  const int r0 = j * T;
+  const int r0 = j * T + hp * BQ;
   const int off = ((b * p.S + r0) * p.Hq + h) * D;
-  const int nv = p.S - r0;
+  const int nv = valid ? p.S - r0 : 0;
   const int nbytes = nv <= 0 ? 0 : ((nv - 1) * rs + D) * 2;
-  const int lrow = ((b * p.Hq + h) * p.N + j) * T;
-  TaskSrc t;
-  t.q = __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)p.q + off), 0, nbytes, 0x00020000);
-  t.o = __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)p.dout + off), 0, nbytes, 0x00020000);
-  t.l = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse2 + lrow), 0, 4 * T, 0x00020000);
-  t.dl = __builtin_amdgcn_make_buffer_rsrc((void*)(p.delta + lrow), 0, 4 * T, 0x00020000);
-  return t;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)p.q + off), 0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)p.dout + off), 0, nbytes, 0x00020000);
+#pragma unroll
+  for (int k = 0; k < PassStage<D, BQ, NW>::KQ; ++k) {
+    const int soff = k * 4 * NW * RPS * rs * 2;
+    st.q[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff, soff, 0);
+    st.o[k] = __builtin_amdgcn_raw_buffer_load_b128(ro, voff, soff, 0);
+  }
+  const int lrow = ((b * p.Hq + h) * p.N + j) * T + hp * BQ;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((w == 0 ? p.lse2 : p.delta) + lrow), 0, valid ? 4 * BQ : 0, 0x00020000);
+  st.l = __builtin_amdgcn_raw_buffer_load_b32(rl, lane * 4, 0, 0);
 }
 
-// Asynchronous copy of pass hp of a task (BQ rows of Q and dO, and their
-// -lse/scale, -Dl) into LDS buffers, as 1 KB direct-to-LDS blocks; wave w
-// issues blocks w, w + NW, ... (the slot pattern of load_tile_async).  voff
-// is the lane's byte offset within a block, (row0 * rs + chunk0 * 8) * 2.
 template <int D, int BQ, int NW>
-__device__ __forceinline__ void load_pass_async(const TaskSrc& ts, int hp, int rs, int voff, char* dq_dst,
-                                                char* do_dst, char* l_dst, int w, int lane) {
-  constexpr int BLK = BQ * 2 * D / 1024;
-  constexpr int RPS = 2 * D == 256 ? 1 : 2;  // rows per 256-byte super-row
-  static_assert(BLK % NW == 0, "whole blocks per wave");
-  const int soff0 = hp * BQ * rs * 2;
+__device__ __forceinline__ void stage_store(const PassStage<D, BQ, NW>& st, char* q_dst, char* o_dst, char* l_dst,
+                                            int w, int lane) {
 #pragma unroll
-  for (int k = 0; k < BLK / NW; ++k) {
-    const int blk = w + k * NW;
-    const int soff = soff0 + k * 4 * NW * RPS * rs * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.q, (lds_void*)(dq_dst + blk * 1024), 16, voff, soff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.o, (lds_void*)(do_dst + blk * 1024), 16, voff, soff, 0, 0);
+  for (int k = 0; k < PassStage<D, BQ, NW>::KQ; ++k) {
+    const int off = (w + k * NW) * 1024 + lane * 16;
+    *reinterpret_cast<f32x4*>(q_dst + off) = st.q[k];
+    *reinterpret_cast<f32x4*>(o_dst + off) = st.o[k];
   }
-  if (w < 2 && (BQ == 64 || lane < BQ))
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? ts.l : ts.dl, (lds_void*)(l_dst + w * 4 * BQ), 4,
-                                             lane * 4, hp * BQ * 4, 0, 0);
+  if (w < 2 && (BQ == 64 || lane < BQ)) *reinterpret_cast<unsigned*>(l_dst + w * 4 * BQ + lane * 4) = st.l;
 }
 
 // ---------------------------------------------------------------------------
@@ -529,7 +537,9 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
                                           const bf16x8* vB, const bf16x8* fkt, f32x16* dK, f32x16* dV,
                                           const Slice& ld, bool ld_on, f32x16& dq_ld, const Slice& prev,
                                           const int* poll_ptr, int poll_expect, int polled, int acc_bytes,
-                                          const BwdParams& p, int rs, bf16* gdq) {
+                                          const BwdParams& p, int rs, bf16* gdq,
+                                          const PassStage<D, BwdCfg<D, T, CAUSAL>::BQ, BwdCfg<D, T, CAUSAL>::NW>* stage,
+                                          bool stage_on, char* st_q, char* st_o, char* st_l, int w) {
   using C = BwdCfg<D, T, CAUSAL>;
   constexpr int QBP = C::QBP;
   // ---- S and dP of the pass's 32-row blocks; the accumulators start at
@@ -581,7 +591,6 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
   }
 
   // ---- dQ of the slice two passes back, next to the softmax
-  const f32x16 dq = dq_products<D, T, CAUSAL>(lS_ld, o, qg, fkt, dq_ld);
   bf16x8 pb[QBP][2], dsb[QBP][2];
 #pragma unroll
   for (int m = 0; m < QBP; ++m) softmax_block(sa[m], pa[m], scale_log2e, pb[m], dsb[m]);
@@ -595,6 +604,15 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
       *reinterpret_cast<bf16*>(lS_cur + o.W(r & 7) + (r >> 3) * 16 * C::RBS + 32 * m * C::RBS) =
           dsb[m][r >> 3][r & 7];
   }
+
+  // ---- dQ of the slice two passes back on top of its loaded partial sum
+  // (late in the pass, so that the loads issued at the end of the previous
+  // pass have had most of this pass to arrive)
+  __builtin_amdgcn_sched_barrier(0);
+  const f32x16 dq = dq_products<D, T, CAUSAL>(lS_ld, o, qg, fkt, dq_ld);
+
+  // ---- the next pass's inputs into the other LDS buffer
+  if (stage_on) stage_store<D, C::BQ, C::NW>(*stage, st_q, st_o, st_l, w, lane);
 
   // ---- store the slice two passes back
   if (ld_on) acc_finish<ATOMIC>(ld, dq, lane, hg, rs, p.scale, gdq);
@@ -665,10 +683,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
 
   // lane's byte offset of its 16-byte slot within a block of Q / dO rows
   const int voffQ = (ldRow0 * rsq + ldChunk0 * 8) * 2;
-#define LOAD_PASS(ts_, hp_, buf_)                                                              \
-  load_pass_async<D, BQ, C::NW>((ts_), (hp_), rsq, voffQ, smem + C::OFF_Q + (buf_) * C::Q_TILE, \
-                                smem + C::OFF_DO + (buf_) * C::Q_TILE,                        \
-                                smem + C::OFF_LD + (buf_) * 2 * 4 * BQ, w, lane)
+  PassStage<D, BQ, C::NW> stage;  // the next pass's inputs on their way to LDS
 
   int gp = 0;        // passes processed by this workgroup (selects the buffers)
   // reduction pipeline: prev = slice of the previous pass (dS in LDS), ld =
@@ -696,18 +711,15 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
     const int b = grp / p.Hkv, hk = grp - b * p.Hkv;
     const int len = item_len(mask, SCHED, N, G, local);
     Task tn = task_at(mask, SCHED, N, G, local, 0);
-    TaskSrc tsn = task_src(p, D, T, b, hk * G + tn.g, tn.j);
-    LOAD_PASS(tsn, 0, gp & 1);
+    stage_load<D, BQ, C::NW>(stage, p, T, b, hk * G + tn.g, tn.j, 0, true, voffQ, w, lane);
+    stage_store<D, BQ, C::NW>(stage, smem + C::OFF_Q + (gp & 1) * C::Q_TILE, smem + C::OFF_DO + (gp & 1) * C::Q_TILE,
+                              smem + C::OFF_LD + (gp & 1) * 2 * 4 * BQ, w, lane);
 
     for (int step = 0; step < len; ++step) {
       const Task t = tn;
-      const TaskSrc ts = tsn;
       const int i = t.i, j = t.j, h = hk * G + t.g;
       const bool has_next = step + 1 < len;
-      if (has_next) {
-        tn = task_at(mask, SCHED, N, G, local, step + 1);
-        tsn = task_src(p, D, T, b, hk * G + tn.g, tn.j);
-      }
+      if (has_next) tn = task_at(mask, SCHED, N, G, local, step + 1);
       if (t.seg_begin) {
         // new KV tile: K through LDS into this wave's K and K^T fragments, V
         // rows straight into registers
@@ -784,9 +796,9 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           wait_vm<4>();
         else
           __builtin_amdgcn_s_waitcnt(0);
-        // the previous pass's LDS writes (dS) are complete once lgkmcnt
-        // drains; no global memory is shared between the waves here, so the
-        // barrier needs no memory fence
+        // the previous pass's LDS writes (dS, the staged inputs) are complete
+        // once lgkmcnt drains; no global memory is shared between the waves
+        // here, so the barrier needs no memory fence
         order_point();
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
         __builtin_amdgcn_s_barrier();
@@ -808,10 +820,11 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
 
         // prefetch the next pass into the other buffer (its readers finished
         // before the barrier above)
-        if (hp + 1 < NP) {
-          LOAD_PASS(ts, hp + 1, buf ^ 1);
-        } else if (has_next) {
-          LOAD_PASS(tsn, 0, buf ^ 1);
+        const bool stage_next = hp + 1 < NP || has_next;
+        {
+          const bool same = hp + 1 < NP;
+          stage_load<D, BQ, C::NW>(stage, p, T, b, same ? h : hk * G + tn.g, same ? j : tn.j, same ? hp + 1 : 0,
+                                   stage_next, voffQ, w, lane);
         }
 
         // this pass's slice
@@ -837,7 +850,10 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         }
         pass_body<D, T, CAUSAL, atomic_dq>(lQ, lO, lL, lS_cur, lS_ld, o, qg, hg, lane, p.scale_log2e, masked, zb,
                                            fk, vB, fkt, dK, dV, ld, have_ld, dq_ld, prev, poll_ptr, poll_expect,
-                                           polled, acc_bytes, p, rsq, gdq);
+                                           polled, acc_bytes, p, rsq, gdq, &stage, stage_next,
+                                           smem + C::OFF_Q + (buf ^ 1) * C::Q_TILE,
+                                           smem + C::OFF_DO + (buf ^ 1) * C::Q_TILE,
+                                           smem + C::OFF_LD + (buf ^ 1) * 2 * 4 * BQ, w);
         acc_tail = true;
         if (have_ld && !atomic_dq) {
           rel = ld;
@@ -915,7 +931,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
       }
     }
   }
-#undef LOAD_PASS
+
 }
 
 // ---------------------------------------------------------------------------
