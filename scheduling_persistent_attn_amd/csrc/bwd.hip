@@ -417,6 +417,7 @@ __device__ __forceinline__ f32x16 dq_products(const char* lS, const LaneOffs<D, 
   for (int kb = 0; kb < C::KBT; ++kb) {
     if (kb + 2 < C::KBT) fa[(kb + 2) % 3] = lds_read16(lS, o.S(kb + 2) + row0);
     c = mfma(fa[kb % 3], fkt[kb], c);
+    __builtin_amdgcn_sched_barrier(0);  // reads stay ahead of their products
   }
   return c;
 }
@@ -587,6 +588,10 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
         sa[m] = mfma(fq[kb % 3][m], fk[kb], sa[m]);
         pa[m] = mfma(fd[kb % 3][m], vB[kb], pa[m]);
       }
+      // (keeps the reads issued for kb + 2 ahead of this step's products;
+      // without it the scheduler sinks each read next to its product and
+      // every product waits for a full LDS round trip)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
