@@ -619,14 +619,15 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
   // ---- the next pass's inputs into the other LDS buffer
   if (stage_on) stage_store<D, C::BQ, C::NW>(*stage, st_q, st_o, st_l, w, lane);
 
-  // ---- store the slice two passes back
-  if (ld_on) acc_finish<ATOMIC>(ld, dq, lane, hg, rs, p.scale, gdq);
-
-  // ---- turn of the previous slice, then its partial sum: these four loads
-  // are the last vector memory operations of the pass (the next pass's
+  // ---- turn of the previous slice (before the stores below are issued:
+  // waiting for the poll then waits for nothing younger), the stores of the
+  // slice two passes back, then the previous slice's partial sum: these four
+  // loads are the last vector memory operations of the pass (the next pass's
   // barrier waits for everything before them)
   order_point();
   if constexpr (!ATOMIC) acquire(poll_ptr, poll_expect, polled, p.ctrl, p.spin_ticks, lane);
+  order_point();
+  if (ld_on) acc_finish<ATOMIC>(ld, dq, lane, hg, rs, p.scale, gdq);
   order_point();
   dq_ld = acc_load(prev.acc, acc_bytes, lane);
   order_point();
@@ -813,14 +814,13 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           rel_pending = false;
         }
 
-        // poll the previous slice's turn counter before the prefetch is
-        // issued, so that waiting for the poll does not wait for the prefetch
-        // (memory operations complete in issue order); without a turn to
-        // take, poll a word that is always zero
+        // the previous slice's turn counter is polled right after the
+        // prefetch below (memory operations complete in issue order: the
+        // prefetch, needed mid-pass, does not wait for the poll); without a
+        // turn to take, poll a word that is always zero
         const bool need_turn = !atomic_dq && have_prev && prev.rank > 0;
         const int* const poll_ptr = need_turn ? prev.cnt : p.ctrl + 3;
         const int poll_expect = need_turn ? prev.rank : 0;
-        const int polled = __hip_atomic_load(poll_ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int acc_bytes = need_turn ? 4096 : 0;
 
         // prefetch the next pass into the other buffer (its readers finished
@@ -831,6 +831,9 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           stage_load<D, BQ, C::NW>(stage, p, T, b, same ? h : hk * G + tn.g, same ? j : tn.j, same ? hp + 1 : 0,
                                    stage_next, voffQ, w, lane);
         }
+        order_point();
+        const int polled = __hip_atomic_load(poll_ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        order_point();
 
         // this pass's slice
         Slice cur;
