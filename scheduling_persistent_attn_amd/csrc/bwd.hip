@@ -629,7 +629,10 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
   order_point();
   if (ld_on) acc_finish<ATOMIC>(ld, dq, lane, hg, rs, p.scale, gdq);
   order_point();
-  dq_ld = acc_load(prev.acc, acc_bytes, lane);
+  if constexpr (ATOMIC)
+    dq_ld = f32x16{};
+  else
+    dq_ld = acc_load(prev.acc, acc_bytes, lane);
   order_point();
 }
 
@@ -797,11 +800,14 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         // this pass's inputs and the previous pass's accumulator stores have
         // completed: everything but the partial-sum loads the previous pass
         // issued last (when it ran a pass body), which the dQ product waits
-        // for itself
-        if (acc_tail)
-          wait_vm<4>();
-        else
-          __builtin_amdgcn_s_waitcnt(0);
+        // for itself.  (The atomic reference publishes nothing, so its
+        // fire-and-forget atomics are not waited for here.)
+        if constexpr (!atomic_dq) {
+          if (acc_tail)
+            wait_vm<4>();
+          else
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         // the previous pass's LDS writes (dS, the staged inputs) are complete
         // once lgkmcnt drains; no global memory is shared between the waves
         // here, so the barrier needs no memory fence
@@ -884,7 +890,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
             acc_finish<atomic_dq>(ld, dq, lane, hg, rsq, p.scale, gdq);
           }
           order_point();
-          __builtin_amdgcn_s_waitcnt(0);
+          if constexpr (!atomic_dq) __builtin_amdgcn_s_waitcnt(0);
           order_point();
           if (!atomic_dq) {
             if (rel_pending) release(rel, lane);
@@ -900,7 +906,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           acc_finish<atomic_dq>(cur, dq, lane, hg, rsq, p.scale, gdq);
           // release: all of this wave's accumulator stores acknowledged first
           order_point();
-          __builtin_amdgcn_s_waitcnt(0);
+          if constexpr (!atomic_dq) __builtin_amdgcn_s_waitcnt(0);
           order_point();
           if (!atomic_dq) release(cur, lane);
           rel_pending = false;
