@@ -13,7 +13,14 @@ after the persistent kernel.  Prints one JSON line.
 The headline value is the whole-step throughput of the fastest deterministic
 schedule in TFLOP/s with FLOPs = 10*B*Hq*S^2*D (halved for a causal mask).  The
 roofline object prices the persistent backward kernel alone (events around
-dash_attn_bwd_run) against the bf16 dense MFMA peak; its traffic figure is the
+dash_attn_bwd_run).  Its bound is the one the kernel's algorithmic intensity
+selects: algorithmic FLOPs over algorithmic bytes (per (KV tile, Q tile) task
+the Q and dO tiles, the two per-row values, and the fp32 dQ partial sum read
+by every contributor but the first and written by every contributor but the
+last; per (batch, KV head, KV tile) K, V, dK and dV; the bf16 dQ) against the
+ridge point 2.5 PFLOP/s / 8 TB/s.  `achieved` is the algorithmic bytes (HBM
+bound) or FLOPs (MFMA bound) of one launch over the kernel's mean duration; the
+fraction of the other peak is reported beside it.  The traffic figure is the
 calibrated FETCH_SIZE + WRITE_SIZE of that kernel read from the committed
 rocprofv3 summary, reported only while that summary's kernel-source hash
 matches the current source.  The cpu_baseline object times the float64 oracle
@@ -32,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "scheduling_persistent_attn_amd", "csrc", "bwd.hip")
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 
 CONFIGS = {
     "llama8b_causal": dict(B=4, S=4096, Hq=32, Hkv=8, D=128, causal=True,
@@ -55,6 +63,20 @@ DEFAULT_CONFIG = "llama8b_causal"
 def flops(cfg):
     f = 10.0 * cfg["B"] * cfg["Hq"] * cfg["S"] ** 2 * cfg["D"]
     return f / 2 if cfg["causal"] else f
+
+
+def algorithmic_bytes(cfg, T):
+    """Bytes one backward launch must move between HBM and the chip under
+    this design (whole tiles; see the module docstring)."""
+    B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    N = (S + T - 1) // T
+    tiles = B * Hq * N                                     # dQ tiles
+    tasks = B * Hq * (N * (N + 1) // 2 if cfg["causal"] else N * N)
+    per_task = 2 * T * D * 2 + 2 * T * 4                   # Q, dO tiles; -lse/scale, -Dl
+    handoff = 2 * (tasks - tiles) * T * D * 4              # fp32 partial sum: load + store
+    dq_out = tiles * T * D * 2
+    kv = B * Hkv * N * 4 * T * D * 2                       # K, V in; dK, dV out
+    return tasks * per_task + handoff + dq_out + kv
 
 
 def log(*a):
@@ -157,6 +179,31 @@ def cpu_baseline(cfg, budget_s=20.0):
                       "own float64 forward" % (groups, B * Hkv, G * groups, S, D, dt)}
 
 
+def roofline(cfg, T, fl, kernel_ms, schedule, traffic):
+    """The persistent kernel against the peak its algorithmic intensity
+    selects (ridge = PEAK_BF16 / PEAK_HBM FLOP per byte)."""
+    nbytes = algorithmic_bytes(cfg, T)
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    tflops = fl / (kernel_ms * 1e-3) / 1e12
+    intensity = fl / nbytes
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    r = {"kernel": "bwd_main (%s)" % schedule,
+         "algorithmic_bytes": nbytes, "algorithmic_flops": fl,
+         "intensity_flop_per_byte": round(intensity, 2), "ridge_flop_per_byte": round(ridge, 2)}
+    if intensity < ridge:
+        r.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                 frac=round(gbs / PEAK_HBM_GBS, 4),
+                 mfma_frac=round(tflops / PEAK_BF16_TFLOPS, 4))
+    else:
+        r.update(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                 frac=round(tflops / PEAK_BF16_TFLOPS, 4),
+                 hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+    # calibrated FETCH_SIZE + WRITE_SIZE bytes per launch (None when the
+    # committed profile predates the kernel source)
+    r["traffic"] = traffic
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,18 +284,8 @@ def main():
         "det_over_atomic": round(bestr["det_over_atomic"], 4) if atomic else None,
         "schedules": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                           for kk, vv in v.items()} for k, v in results.items()},
-        "roofline": {
-            "bound": "mfma",
-            # algorithmic FLOPs of one launch / mean event-timed duration of
-            # the persistent kernel (events around dash_attn_bwd_run)
-            "kernel": "bwd_main (%s)" % best,
-            "achieved": round(bestr["kernel_tflops"], 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(bestr["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
-            # calibrated FETCH_SIZE + WRITE_SIZE bytes per launch
-            "traffic": committed_traffic(args.config, best),
-        },
+        "roofline": roofline(cfg, T, fl, bestr["kernel_ms_mean"], best,
+                             committed_traffic(args.config, best)),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)

@@ -28,7 +28,8 @@
 //   dK^T += Q^T dS        A = Q^T  (transposing LDS reads), B = dS (registers)
 //   dS -> LDS
 // and per wave a 32-column slice of dQ = dS K with A = dS (LDS) and B = K^T
-// (transposing LDS reads), followed by the ordered reduction.
+// fragments held in registers for the whole run of the KV tile (formed once by
+// transposing LDS reads), followed by the ordered reduction.
 // All products use v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulate).
 // The 32x32 accumulator holds column n = lane % 32 and rows
 // 8*(r/4) + 4*(lane/32) + r%4 in register r; a product whose contraction runs
@@ -312,17 +313,18 @@ __device__ __forceinline__ void stage_store(const PassStage<D, BQ, NW>& st, char
 // KV tile stay in registers for the whole run of the tile: the K and V rows
 // it owns (B operands of S and dP) and the K^T fragments of its dQ feature
 // block (B operand of dQ = dS K); the K tile passes through LDS once per run
-// to form them.  Q/dO and the per-row -lse/scale, -Dl values of a pass are
-// double-buffered in LDS (the next pass is copied in while the current one
-// computes), and so is dS: the dQ product of pass p-1, which needs every
-// wave's dS, runs during pass p next to that pass's softmax, so one workgroup
-// barrier per pass suffices and the matrix cores have independent work while
-// the vector units evaluate exp2.  The ordered reduction of pass p-1's slice
-// is spread over pass p: its turn counter is polled at the start, the
-// accumulator loads are issued after the first products and the add and
-// store come at the end, so the round trips to the device-coherent level
-// overlap with computation.  The last pass of a KV tile's run finishes its
-// own dQ and reduction before the tile changes.
+// to form them.  The next pass's Q/dO rows and per-row -lse/scale, -Dl values
+// are loaded into registers at the start of a pass and written into the other
+// half of a double buffer in LDS late in it.  dS is triple-buffered: the dQ
+// product of a slice, which needs every wave's dS, is formed two passes after
+// that dS was written, so one workgroup barrier per pass suffices.  The
+// ordered reduction of a slice is pipelined over the three passes that follow
+// it: at the end of the first its turn (polled early in that pass) is checked
+// and its partial sum loaded; in the second its product is added and stored
+// (or, by the last contributor, written to dq in bf16); after the barrier of
+// the third its counter is published.  The round trips to the device-coherent
+// level thus overlap with whole passes of computation.  The last pass of a KV
+// tile's run finishes the open slices before the tile changes.
 template <int D, int T, bool CAUSAL>
 struct BwdCfg {
   static constexpr int NW = T / 32;      // waves; wave w owns keys [32w, 32w+32)
