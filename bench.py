@@ -287,6 +287,11 @@ def main():
         "roofline": roofline(cfg, T, fl, bestr["kernel_ms_mean"], best,
                              committed_traffic(args.config, best)),
     }
+    # the schedule the simulator picks for this shape on this device (AUTO)
+    names = {v: k for k, v in dash.SCHEDULES.items()}
+    auto = names[dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, 1 if cfg["causal"] else 0)]
+    line["auto_schedule"] = auto
+    line["auto_is_measured_best"] = auto == best
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
         line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 6)

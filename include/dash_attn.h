@@ -62,13 +62,18 @@ enum dash_mask { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 };
  *  ATOMIC           NOT deterministic: dQ reduced with unordered fp32 atomic
  *                   adds (the non-deterministic counterpart of section 1);
  *                   kept only as the speed reference.
+ *  AUTO             one of the four deterministic schedules, chosen per shape
+ *                   and device by the schedule simulator below (see
+ *                   dash_attn_bwd_auto_schedule); deterministic like the
+ *                   schedule it resolves to.
  */
 enum dash_schedule {
   DASH_SCHED_NAIVE = 0,
   DASH_SCHED_DESCENDING_Q = 1,
   DASH_SCHED_SHIFT = 2,
   DASH_SCHED_SYMMETRIC_SHIFT = 3,
-  DASH_SCHED_ATOMIC = 4
+  DASH_SCHED_ATOMIC = 4,
+  DASH_SCHED_AUTO = 5
 };
 
 enum dash_status {
@@ -163,6 +168,18 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v,
  * error, else DASH_OK.  Reads 8 bytes of the workspace. */
 int dash_attn_bwd_check(const void* workspace, void* stream);
 
+/* The deterministic schedule that DASH_SCHED_AUTO resolves to for these
+ * arguments on the current device, or minus a dash_status.  The choice is
+ * dash_sim_select over the device's persistent grid (P = the workgroups
+ * dash_attn_bwd launches, dynamic dispatch), B*Hkv groups of Hq/Hkv query
+ * heads on the tile count of (S, D), with weights c_full = c_diag = 1 (the
+ * kernel computes a causal diagonal tile in full) and r = 0.1 (the exposed
+ * part of a hand-off, relative to one task); SHIFT and SYMMETRIC_SHIFT are
+ * candidates only when one group of items fits in the grid.  The result is
+ * cached per device and shape, so a given shape on a given device always
+ * runs the same schedule: AUTO keeps the determinism contract. */
+int dash_attn_bwd_auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask);
+
 /* Static description of a status code. */
 const char* dash_status_string(int status);
 
@@ -220,6 +237,18 @@ typedef struct {
 int dash_sim_run(int mask, int schedule, int N, int G, int groups, int P,
                  int dispatch, double c_full, double c_diag, double r,
                  dash_sim_result* out);
+
+/* Schedule selection by critical path (NEXT step of the pages' section 2:
+ * pick the strategy per shape and hardware).  Simulates every deterministic
+ * schedule that applies to the mask and N (SYMMETRIC_SHIFT only for causal
+ * masks and even N), skips those that deadlock on P workers, and writes the
+ * one with the shortest critical path to *schedule (ties go to the earlier of
+ * SYMMETRIC_SHIFT, SHIFT, DESCENDING_Q, NAIVE) and its report to *out (may be
+ * NULL).  Returns DASH_ERR_UNSUPPORTED when every candidate deadlocks, and the
+ * argument errors of dash_sim_run. */
+int dash_sim_select(int mask, int N, int G, int groups, int P, int dispatch,
+                    double c_full, double c_diag, double r, int* schedule,
+                    dash_sim_result* out);
 
 #ifdef __cplusplus
 }

@@ -219,3 +219,28 @@ def simulate(schedule, mask, N, G=1, groups=1, P=None, dispatch="static",
     res["efficiency"] = (total / (used * res["makespan"])
                          if res["makespan"] not in (0.0, float("inf")) else 0.0)
     return res
+
+
+# Candidates of the schedule selection, in the order that breaks ties (the
+# first one wins on an equal critical path).
+SELECT_ORDER = (sch.SYMMETRIC_SHIFT, sch.SHIFT, sch.DESCENDING_Q, sch.NAIVE)
+
+
+def select(mask, N, G=1, groups=1, P=None, dispatch="static", c=1.0, c_diag=None, r=0.0):
+    """The deterministic schedule with the shortest critical path for this
+    shape and worker count (DASH technical summary, section 2: the schedule
+    is chosen to minimise the DAG's critical path; the pages leave the choice
+    per shape and hardware to the practitioner).  Schedules that deadlock on P
+    workers, or do not apply to the mask and tile count, are skipped.
+    Returns (schedule, simulate() result)."""
+    best = None
+    for s in SELECT_ORDER:
+        if s == sch.SYMMETRIC_SHIFT and (mask != sch.CAUSAL or N % 2):
+            continue
+        res = simulate(s, mask, N, G=G, groups=groups, P=P, dispatch=dispatch,
+                       c=c, c_diag=c_diag, r=r)
+        if res["deadlock"]:
+            continue
+        if best is None or res["makespan"] < best[1]["makespan"]:
+            best = (s, res)
+    return best

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdash_attn.so")
 
 MASK_FULL, MASK_CAUSAL = 0, 1
-NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT, ATOMIC = 0, 1, 2, 3, 4
+NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT, ATOMIC, AUTO = 0, 1, 2, 3, 4, 5
 SCHEDULES = {"naive": NAIVE, "descending_q": DESCENDING_Q, "shift": SHIFT,
              "symmetric_shift": SYMMETRIC_SHIFT, "atomic": ATOMIC}
 DETERMINISTIC = (NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT)
@@ -31,7 +31,8 @@ SYMBOLS = (
     "dash_attn_tile_size", "dash_attn_bwd_workspace_size", "dash_attn_fwd",
     "dash_attn_bwd", "dash_attn_bwd_prepare", "dash_attn_bwd_run", "dash_attn_bwd_check", "dash_status_string",
     "dash_attn_bwd_grid_size", "dash_schedule_num_items",
-    "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run",
+    "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
+    "dash_attn_bwd_auto_schedule",
 )
 
 
@@ -90,6 +91,11 @@ def lib():
     L.dash_schedule_task.restype = i
     L.dash_sim_run.argtypes = [i] * 7 + [d, d, d, ctypes.POINTER(SimResult)]
     L.dash_sim_run.restype = i
+    L.dash_sim_select.argtypes = [i] * 6 + [d, d, d, ctypes.POINTER(ctypes.c_int),
+                                            ctypes.POINTER(SimResult)]
+    L.dash_sim_select.restype = i
+    L.dash_attn_bwd_auto_schedule.argtypes = [i] * 6
+    L.dash_attn_bwd_auto_schedule.restype = i
     _lib = L
     return L
 
@@ -128,6 +134,28 @@ def dash_schedule_task(mask, schedule, N, G, item, step):
     if st != 0:
         raise ValueError("task out of range")
     return g.value, i.value, j.value, r.value
+
+
+def dash_sim_select(mask, N, G=1, groups=1, P=256, dispatch=1, c_full=1.0, c_diag=None, r=0.0):
+    """(schedule, report) of the deterministic schedule with the shortest
+    simulated critical path."""
+    if c_diag is None:
+        c_diag = c_full
+    sched = ctypes.c_int(-1)
+    out = SimResult()
+    st = lib().dash_sim_select(mask, N, G, groups, P, dispatch, float(c_full), float(c_diag),
+                               float(r), ctypes.byref(sched), ctypes.byref(out))
+    if st != DASH_OK:
+        raise DashError(st, "dash_sim_select")
+    return sched.value, out.as_dict()
+
+
+def dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, mask):
+    """The schedule AUTO runs for this shape on the current device."""
+    r = lib().dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, mask)
+    if r < 0:
+        raise DashError(-r, "dash_attn_bwd_auto_schedule")
+    return r
 
 
 def dash_sim_run(mask, schedule, N, G=1, groups=1, P=256, dispatch=1,

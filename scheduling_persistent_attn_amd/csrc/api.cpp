@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/dash_attn.h"
 #include "kernels.h"
@@ -65,7 +66,7 @@ int check_shape(int B, int Hq, int Hkv, int S, int D, int mask, int schedule) {
   if (Hq % Hkv != 0) return DASH_ERR_SHAPE;
   if (D != 64 && D != 128) return DASH_ERR_UNSUPPORTED;
   if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return DASH_ERR_SCHEDULE_MASK;
-  if (schedule < DASH_SCHED_NAIVE || schedule > DASH_SCHED_ATOMIC) return DASH_ERR_SCHEDULE_MASK;
+  if (schedule < DASH_SCHED_NAIVE || schedule > DASH_SCHED_AUTO) return DASH_ERR_SCHEDULE_MASK;
   return DASH_OK;
 }
 
@@ -97,9 +98,72 @@ int make_layout(int B, int Hq, int S, int D, Layout* L) {
   return DASH_OK;
 }
 
+// Weights of the schedule simulator for DASH_SCHED_AUTO, per task: a full
+// tile and a causal diagonal tile cost the same in this kernel (the diagonal
+// is computed whole and masked), and the part of a dQ hand-off that stays
+// exposed is about a tenth of a task (it is pipelined behind later passes).
+constexpr double kAutoC = 1.0, kAutoCDiag = 1.0, kAutoR = 0.1;
+
+struct AutoEntry {
+  int dev, B, Hq, Hkv, S, D, mask, schedule;
+};
+std::vector<AutoEntry> g_auto;
+std::mutex g_auto_mu;
+
+// Resolves DASH_SCHED_AUTO for a shape on the current device (cached).
+int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
+  int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_NAIVE);
+  if (st != DASH_OK) return st;
+  Layout L;
+  st = make_layout(B, Hq, S, D, &L);
+  if (st != DASH_OK) return st;
+  if (B == 0 || S == 0) {
+    *out = DASH_SCHED_NAIVE;
+    return DASH_OK;
+  }
+  DeviceInfo* dev = nullptr;
+  st = device_info(&dev);
+  if (st != DASH_OK) return st;
+  int dev_id = 0;
+  if (hipGetDevice(&dev_id) != hipSuccess) return DASH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_auto_mu);
+  for (const AutoEntry& e : g_auto)
+    if (e.dev == dev_id && e.B == B && e.Hq == Hq && e.Hkv == Hkv && e.S == S && e.D == D &&
+        e.mask == mask) {
+      *out = e.schedule;
+      return DASH_OK;
+    }
+  const int grid = dev->cus * dev->bpc[D == 128][L.T == 128][mask];
+  if (grid <= 0) return DASH_ERR_HIP;
+  int sched = -1;
+  st = dash_sim_select(mask, L.N, Hq / Hkv, B * Hkv, grid, 1, kAutoC, kAutoCDiag, kAutoR, &sched,
+                       nullptr);
+  if (st == DASH_ERR_UNSUPPORTED || st == DASH_ERR_SCHEDULE_MASK) {
+    // too large to simulate: the simulator's usual order on co-resident
+    // groups, else the descending order (causal) or the naive one
+    const bool sym_ok = mask == DASH_MASK_CAUSAL && L.N % 2 == 0 &&
+                        dash::items_per_group(DASH_SCHED_SYMMETRIC_SHIFT, L.N) <= grid;
+    const bool shift_ok = dash::items_per_group(DASH_SCHED_SHIFT, L.N) <= grid;
+    sched = sym_ok ? DASH_SCHED_SYMMETRIC_SHIFT
+                   : shift_ok ? DASH_SCHED_SHIFT
+                              : mask == DASH_MASK_CAUSAL ? DASH_SCHED_DESCENDING_Q : DASH_SCHED_NAIVE;
+  } else if (st != DASH_OK) {
+    return st;
+  }
+  g_auto.push_back({dev_id, B, Hq, Hkv, S, D, mask, sched});
+  *out = sched;
+  return DASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int dash_attn_bwd_auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask) {
+  int sched = 0;
+  const int st = auto_schedule(B, Hq, Hkv, S, D, mask, &sched);
+  return st == DASH_OK ? sched : -st;
+}
 
 int dash_attn_tile_size(int S, int D) {
   if (D == 64) return S <= 512 ? 64 : 128;
@@ -205,6 +269,10 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
     return DASH_ERR_WORKSPACE;
 
+  if (schedule == DASH_SCHED_AUTO) {
+    st = auto_schedule(B, Hq, Hkv, S, D, mask, &schedule);
+    if (st != DASH_OK) return st;
+  }
   DeviceInfo* dev = nullptr;
   st = device_info(&dev);
   if (st != DASH_OK) return st;
@@ -277,10 +345,10 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return DASH_OK;
 }
 
-int launch_main_phase(const BwdPlan& P, int D, int mask, int schedule, hipStream_t s) {
+int launch_main_phase(const BwdPlan& P, int D, int mask, hipStream_t s) {
   if (dash::launch_bwd_main(D, P.L.T, mask == DASH_MASK_CAUSAL, P.bp, P.grid, s) != hipSuccess)
     return DASH_ERR_HIP;
-  if (schedule == DASH_SCHED_ATOMIC &&
+  if (P.bp.schedule == DASH_SCHED_ATOMIC &&
       dash::launch_finalize_atomic(D, P.L.T, P.fp, s) != hipSuccess)
     return DASH_ERR_HIP;
   return DASH_OK;
@@ -301,7 +369,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   if (st != DASH_OK || empty) return st;
   hipStream_t s = (hipStream_t)stream;
   if (dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
-  return launch_main_phase(P, D, mask, schedule, s);
+  return launch_main_phase(P, D, mask, s);
 }
 
 int dash_attn_bwd_prepare(const void* o, const void* dout, const float* lse, int B, int Hq,
@@ -324,7 +392,7 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v, const void* d
   int st = plan_bwd(q, k, v, nullptr, dout, nullptr, dq, dk, dv, B, Hq, Hkv, S, D, mask,
                     schedule, workspace, workspace_bytes, 2, &P, &empty);
   if (st != DASH_OK || empty) return st;
-  return launch_main_phase(P, D, mask, schedule, (hipStream_t)stream);
+  return launch_main_phase(P, D, mask, (hipStream_t)stream);
 }
 
 int dash_attn_bwd_check(const void* workspace, void* stream) {

@@ -288,3 +288,32 @@ extern "C" int dash_sim_run(int mask, int schedule, int N, int G, int groups, in
   *out = res;
   return DASH_OK;
 }
+
+// The deterministic schedule with the shortest critical path for a shape and
+// worker count: every candidate that applies to the mask and tile count is
+// simulated, deadlocked ones are skipped, and ties go to the earlier
+// candidate of {SYMMETRIC_SHIFT, SHIFT, DESCENDING_Q, NAIVE}.
+extern "C" int dash_sim_select(int mask, int N, int G, int groups, int P, int dispatch,
+                               double c_full, double c_diag, double r, int* schedule,
+                               dash_sim_result* out) {
+  if (!schedule) return DASH_ERR_NULL;
+  static const int order[4] = {DASH_SCHED_SYMMETRIC_SHIFT, DASH_SCHED_SHIFT,
+                               DASH_SCHED_DESCENDING_Q, DASH_SCHED_NAIVE};
+  int best = -1;
+  dash_sim_result best_res = {};
+  for (int s : order) {
+    if (s == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || N % 2 != 0)) continue;
+    dash_sim_result res;
+    const int st = dash_sim_run(mask, s, N, G, groups, P, dispatch, c_full, c_diag, r, &res);
+    if (st != DASH_OK) return st;
+    if (res.deadlock) continue;
+    if (best < 0 || res.makespan < best_res.makespan) {
+      best = s;
+      best_res = res;
+    }
+  }
+  if (best < 0) return DASH_ERR_UNSUPPORTED;
+  *schedule = best;
+  if (out) *out = best_res;
+  return DASH_OK;
+}

@@ -212,3 +212,60 @@ def test_phase_validation_before_device():
     bad = list(args)
     bad[14] = None
     assert L.dash_attn_bwd_run(*bad) == dash.DASH_ERR_WORKSPACE
+
+
+SELECT_CASES = [
+    # mask, N, G, groups, P, dispatch, c, c_diag, r
+    (sch.FULL, 4, 1, 1, 4, 0, 4.0, 4.0, 1.0),
+    (sch.FULL, 4, 1, 2, 3, 1, 4.0, 4.0, 1.0),     # shift cannot keep a group resident
+    (sch.FULL, 6, 2, 2, 12, 1, 5.0, 5.0, 0.5),
+    (sch.CAUSAL, 4, 1, 1, 2, 0, 4.0, 2.0, 1.0),
+    (sch.CAUSAL, 6, 3, 2, 8, 1, 5.0, 3.0, 1.0),
+    (sch.CAUSAL, 5, 2, 3, 6, 1, 1.0, 1.0, 0.1),  # odd N: no symmetric shift
+    (sch.CAUSAL, 8, 1, 4, 3, 1, 1.0, 1.0, 0.1),
+    (sch.CAUSAL, 8, 4, 2, 16, 1, 1.0, 1.0, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES)
+def test_library_selection_equals_oracle(case):
+    m, N, G, groups, P, disp, c, cd, r = case
+    ref = dag.select(m, N, G=G, groups=groups, P=P, dispatch="dynamic" if disp else "static",
+                     c=c, c_diag=cd, r=r)
+    if ref is None:
+        with pytest.raises(dash.DashError):
+            dash.dash_sim_select(m, N, G, groups, P, disp, c, cd, r)
+        return
+    sched, res = dash.dash_sim_select(m, N, G, groups, P, disp, c, cd, r)
+    assert sched == ref[0]
+    assert res["makespan"] == ref[1]["makespan"]
+
+
+def test_selection_closed_forms():
+    # one group, one worker per chain, full mask: shift reaches N(c + r), the
+    # naive order pays (N - 1) r more (the critical paths pinned above)
+    N, c, r = 16, 4.0, 1.0
+    sched, res = dash.dash_sim_select(sch.FULL, N, 1, 1, N, 0, c, c, r)
+    assert sched == sch.SHIFT and res["makespan"] == N * (c + r)
+    # causal, even N, N/2 workers: the symmetric pairs finish in (N + 1)(c + r),
+    # against N (c + r) + (N - 1) r at least for one-chain-per-worker orders
+    sched, res = dash.dash_sim_select(sch.CAUSAL, N, 1, 1, N // 2, 0, c, c, r)
+    assert sched == sch.SYMMETRIC_SHIFT and res["makespan"] == (N + 1) * (c + r)
+    # fewer workers than a group's chains: the shift family deadlocks and is
+    # never chosen
+    sched, _ = dash.dash_sim_select(sch.FULL, N, 1, 1, N // 2, 1, c, c, r)
+    assert sched in (sch.NAIVE, sch.DESCENDING_Q)
+
+
+def test_auto_schedule_arguments():
+    L = dash.lib()
+    assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, dash.AUTO) == \
+        dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, dash.NAIVE)
+    assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, 6) == 0
+    assert L.dash_attn_bwd_auto_schedule(1, 3, 2, 256, 64, 1) == -dash.DASH_ERR_SHAPE
+    assert L.dash_attn_bwd_auto_schedule(1, 2, 2, 256, 64, 2) == -dash.DASH_ERR_SCHEDULE_MASK
+    assert L.dash_attn_bwd_auto_schedule(0, 2, 2, 256, 64, 1) == dash.NAIVE  # empty
+    # argument errors come before the device is needed to resolve AUTO
+    assert _bwd(sched=dash.AUTO, q=None) == dash.DASH_ERR_NULL
+    assert _bwd(sched=dash.AUTO, ws=None) == dash.DASH_ERR_WORKSPACE
+    assert _bwd(sched=dash.AUTO, S=0, q=None, ws=None) == dash.DASH_OK

@@ -221,3 +221,24 @@ def test_lemma1_violation_changes_critical_path():
     # an order edge whose source is deeper than its target lengthens the path
     res = dag.simulate(sch.NAIVE, sch.FULL, 4, c=4.0, r=1.0)
     assert res["violations"] > 0 and res["makespan"] > res["base_makespan"]
+
+
+def test_oracle_selection_closed_forms():
+    # selection = the schedule of least critical path; pinned on shapes whose
+    # critical paths have closed forms (one group, one chain per worker)
+    from oracle import dag
+    N, c, r = 8, 4.0, 1.0
+    s, res = dag.select(sch.FULL, N, P=N, c=c, r=r)
+    assert s == sch.SHIFT and res["makespan"] == N * (c + r)
+    s, res = dag.select(sch.CAUSAL, N, P=N // 2, c=c, r=r)
+    assert s == sch.SYMMETRIC_SHIFT and res["makespan"] == (N + 1) * (c + r)
+    # odd N, causal: the symmetric shift does not apply
+    s, _ = dag.select(sch.CAUSAL, 5, P=5, c=c, r=r)
+    assert s != sch.SYMMETRIC_SHIFT
+    # a deadlocked candidate is never chosen
+    s, _ = dag.select(sch.FULL, N, P=N // 2, dispatch="dynamic", c=c, r=r)
+    assert s in (sch.NAIVE, sch.DESCENDING_Q)
+    # ties go to the earlier candidate: with r = 0 every order of a full mask
+    # on one chain per worker takes N c
+    s, res = dag.select(sch.FULL, N, P=N, c=c, r=0.0)
+    assert s == sch.SHIFT and res["makespan"] == N * c
