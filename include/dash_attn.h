@@ -61,7 +61,11 @@ enum dash_mask { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 };
  *                   (section 2.2 B, symmetric shift).
  *  ATOMIC           NOT deterministic: dQ reduced with unordered fp32 atomic
  *                   adds (the non-deterministic counterpart of section 1);
- *                   kept only as the speed reference.
+ *                   kept only as the speed reference.  Its items are the
+ *                   symmetric pairs on causal masks with an even tile count
+ *                   (the best-balanced items; its result does not depend on
+ *                   the order), one chain per KV tile otherwise; ranks are
+ *                   reported in ascending KV order.
  *  AUTO             one of the four deterministic schedules, chosen per shape
  *                   and device by the schedule simulator below (see
  *                   dash_attn_bwd_auto_schedule); deterministic like the

@@ -32,6 +32,12 @@ Schedules (DASH technical summary, section 2.2):
   shift; phase 2 is the remaining two triangles, folded so that pair p first
   takes Q tiles p..N/2-1 of KV p and then Q tiles N-1 down to N-1-p of KV
   N-1-p.  Reduction order = lockstep arrival order.
+* ATOMIC -- the non-deterministic counterpart (section 1: unordered atomic
+  adds into dQ).  The pages give it no order, and its result does not depend
+  on one.  Reading used here: it takes the best-balanced items for the mask,
+  the symmetric pairs on causal masks with an even tile count and one chain
+  per KV tile otherwise, so that a comparison with the ordered schedules
+  isolates the reduction; its ranks are listed in ascending KV order.
 
 Grouped-query attention: Hq/Hkv = G query heads read one KV head.  One item
 serves one KV tile (or pair) for all G query heads so that dK/dV stay
@@ -104,7 +110,11 @@ def items(schedule, mask, N, G=1):
     tile i, Q tile j.
     """
     out = []
-    if schedule == SYMMETRIC_SHIFT:
+    # the atomic reference's result does not depend on its order; on causal
+    # masks with an even tile count it takes the symmetric pairs (the
+    # best-balanced items), else one chain per KV tile
+    paired = schedule == SYMMETRIC_SHIFT or (schedule == ATOMIC and mask == CAUSAL and N % 2 == 0)
+    if paired:
         if mask != CAUSAL:
             raise ValueError("symmetric shift is defined for causal masks")
         for p in range(N // 2):

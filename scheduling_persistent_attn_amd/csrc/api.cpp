@@ -142,8 +142,8 @@ int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
     // too large to simulate: the simulator's usual order on co-resident
     // groups, else the descending order (causal) or the naive one
     const bool sym_ok = mask == DASH_MASK_CAUSAL && L.N % 2 == 0 &&
-                        dash::items_per_group(DASH_SCHED_SYMMETRIC_SHIFT, L.N) <= grid;
-    const bool shift_ok = dash::items_per_group(DASH_SCHED_SHIFT, L.N) <= grid;
+                        dash::items_per_group(mask, DASH_SCHED_SYMMETRIC_SHIFT, L.N) <= grid;
+    const bool shift_ok = dash::items_per_group(mask, DASH_SCHED_SHIFT, L.N) <= grid;
     sched = sym_ok ? DASH_SCHED_SYMMETRIC_SHIFT
                    : shift_ok ? DASH_SCHED_SHIFT
                               : mask == DASH_MASK_CAUSAL ? DASH_SCHED_DESCENDING_Q : DASH_SCHED_NAIVE;
@@ -280,7 +280,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   const int grid = dev->cus * bpc;
   if (grid <= 0) return DASH_ERR_HIP;
   const int G = Hq / Hkv;
-  const int ipg = dash::items_per_group(schedule, L.N);
+  const int ipg = dash::items_per_group(mask, schedule, L.N);
   // The shift family waits on chains that come later in the dispatch order,
   // so a whole group of items must be able to run at once.
   if ((schedule == DASH_SCHED_SHIFT || schedule == DASH_SCHED_SYMMETRIC_SHIFT) && ipg > grid)
@@ -408,7 +408,7 @@ int dash_attn_bwd_check(const void* workspace, void* stream) {
 int dash_schedule_num_items(int mask, int schedule, int N) {
   if (N < 1 || (mask != 0 && mask != 1) || schedule < 0 || schedule > 4) return -1;
   if (schedule == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || N % 2)) return -1;
-  return dash::items_per_group(schedule, N);
+  return dash::items_per_group(mask, schedule, N);
 }
 
 int dash_schedule_item_len(int mask, int schedule, int N, int G, int item) {

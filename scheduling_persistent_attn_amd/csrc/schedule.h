@@ -46,15 +46,22 @@ struct Task {
   int seg_end;    // last task of that run
 };
 
-DASH_HD int items_per_group(int schedule, int N) {
-  return schedule == SCHED_SYM ? N / 2 : N;
+// Items built from the symmetric pairs of section 2.2 B: the symmetric shift,
+// and the atomic reference on causal masks with an even tile count (its
+// result does not depend on the order, so it takes the best-balanced items).
+DASH_HD bool paired_items(int mask, int schedule, int N) {
+  return schedule == SCHED_SYM || (schedule == SCHED_ATOMIC && mask == MASK_CAUSAL && N % 2 == 0);
+}
+
+DASH_HD int items_per_group(int mask, int schedule, int N) {
+  return paired_items(mask, schedule, N) ? N / 2 : N;
 }
 
 // Tasks of one KV chain per query head.
 DASH_HD int chain_len(int mask, int N, int i) { return mask == MASK_CAUSAL ? N - i : N; }
 
 DASH_HD int item_len(int mask, int schedule, int N, int G, int item) {
-  if (schedule == SCHED_SYM) return G * (N + 1);
+  if (paired_items(mask, schedule, N)) return G * (N + 1);
   return G * chain_len(mask, N, item);
 }
 
@@ -63,7 +70,7 @@ DASH_HD int contributors(int mask, int N, int j) { return mask == MASK_CAUSAL ? 
 
 DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
   Task t;
-  if (schedule == SCHED_SYM) {
+  if (paired_items(mask, schedule, N)) {
     const int h = N / 2, p = item;
     const int len_a = G * (N - p);  // phase 1 + KV-p part of phase 2
     if (step < len_a) {
@@ -92,6 +99,8 @@ DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
       t.j = N - 1 - s;
       t.rank = t.i;
     }
+    // the atomic reference keeps the ascending key/value order of ranks
+    if (schedule == SCHED_ATOMIC) t.rank = t.i;
     return t;
   }
   const int i = item;

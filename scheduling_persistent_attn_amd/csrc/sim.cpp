@@ -42,7 +42,7 @@ struct Problem {
 };
 
 bool build(Problem& pb) {
-  const int ipg = dash::items_per_group(pb.schedule, pb.N);
+  const int ipg = dash::items_per_group(pb.mask, pb.schedule, pb.N);
   const int items = ipg * pb.groups;
   pb.item_first.assign(items + 1, 0);
   for (int grp = 0; grp < pb.groups; ++grp) {
