@@ -425,25 +425,40 @@ __device__ __forceinline__ f32x16 dq_products(const char* lS, const LaneOffs<D, 
 }
 
 // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows of block m of the
-// pass, fragments one step ahead.
+// pass, fragments two steps ahead, with the block's dS element writes to lS
+// spread over the steps (a scheduling barrier per step keeps that order).
 template <int D, int T, bool CAUSAL>
 __device__ __forceinline__ void dvdk_block(const char* lQ, const char* lO, const LaneOffs<D, T>& o, int m,
-                                           const bf16x8* pb, const bf16x8* dsb, f32x16* dK, f32x16* dV) {
+                                           const bf16x8* pb, const bf16x8* dsb, f32x16* dK, f32x16* dV,
+                                           char* lS) {
   using C = BwdCfg<D, T, CAUSAL>;
-  bf16x8 fa[2], fb[2];
-  fa[0] = lds_read_tr(lO, o.Tq(0, 0) + 32 * m * C::RBD, o.Tq(0, 1) + 32 * m * C::RBD);
-  fb[0] = lds_read_tr(lQ, o.Tq(0, 0) + 32 * m * C::RBD, o.Tq(0, 1) + 32 * m * C::RBD);
+  constexpr int X = 2 * C::DB;       // product steps
+  constexpr int WPS = 16 / X;        // dS element writes per step
+  bf16x8 fa[3], fb[3];
 #pragma unroll
-  for (int x = 0; x < 2 * C::DB; ++x) {
+  for (int x = 0; x < 2; ++x) {
     const int md = x >> 1, kq = x & 1;
-    if (x + 1 < 2 * C::DB) {
-      const int md1 = (x + 1) >> 1, kq1 = (x + 1) & 1;
-      const int base = (32 * m + 16 * kq1) * C::RBD;
-      fa[(x + 1) & 1] = lds_read_tr(lO, o.Tq(md1, 0) + base, o.Tq(md1, 1) + base);
-      fb[(x + 1) & 1] = lds_read_tr(lQ, o.Tq(md1, 0) + base, o.Tq(md1, 1) + base);
+    const int base = (32 * m + 16 * kq) * C::RBD;
+    fa[x] = lds_read_tr(lO, o.Tq(md, 0) + base, o.Tq(md, 1) + base);
+    fb[x] = lds_read_tr(lQ, o.Tq(md, 0) + base, o.Tq(md, 1) + base);
+  }
+#pragma unroll
+  for (int x = 0; x < X; ++x) {
+    const int md = x >> 1, kq = x & 1;
+    if (x + 2 < X) {
+      const int md2 = (x + 2) >> 1, kq2 = (x + 2) & 1;
+      const int base = (32 * m + 16 * kq2) * C::RBD;
+      fa[(x + 2) % 3] = lds_read_tr(lO, o.Tq(md2, 0) + base, o.Tq(md2, 1) + base);
+      fb[(x + 2) % 3] = lds_read_tr(lQ, o.Tq(md2, 0) + base, o.Tq(md2, 1) + base);
     }
-    dV[md] = mfma(fa[x & 1], pb[kq], dV[md]);
-    dK[md] = mfma(fb[x & 1], dsb[kq], dK[md]);
+    dV[md] = mfma(fa[x % 3], pb[kq], dV[md]);
+    dK[md] = mfma(fb[x % 3], dsb[kq], dK[md]);
+#pragma unroll
+    for (int e = 0; e < WPS; ++e) {
+      const int r = x * WPS + e;
+      *reinterpret_cast<bf16*>(lS + o.W(r & 7) + (r >> 3) * 16 * C::RBS + 32 * m * C::RBS) = dsb[r >> 3][r & 7];
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -605,11 +620,7 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
   // ---- dV^T += dO^T P, dK^T += Q^T dS; dS -> LDS
 #pragma unroll
   for (int m = 0; m < QBP; ++m) {
-    dvdk_block<D, T, CAUSAL>(lQ, lO, o, m, pb[m], dsb[m], dK, dV);
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      *reinterpret_cast<bf16*>(lS_cur + o.W(r & 7) + (r >> 3) * 16 * C::RBS + 32 * m * C::RBS) =
-          dsb[m][r >> 3][r & 7];
+    dvdk_block<D, T, CAUSAL>(lQ, lO, o, m, pb[m], dsb[m], dK, dV, lS_cur);
   }
 
   // ---- dQ of the slice two passes back on top of its loaded partial sum
