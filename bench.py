@@ -36,7 +36,16 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(ROOT, "scheduling_persistent_attn_amd", "csrc", "bwd.hip")
+# the sources the persistent kernel is compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "scheduling_persistent_attn_amd", "csrc", f)
+                  for f in ("bwd.hip", "schedule.h", "kernels.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
@@ -138,7 +147,7 @@ def committed_traffic(config, schedule):
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     if not m:
         return None
-    if hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest() != m.group(1):
+    if kernel_source_hash() != m.group(1):
         return None
     m = re.search(r"traffic_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" % re.escape(schedule), text)
     return float(m.group(1)) if m else None
