@@ -242,7 +242,18 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        # and the rate of the same copy, for scale (bytes read + written)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3,
+                          "copy_ms": round(ms, 4), "copy_read_write_TBps": round(2 * n / ms / 1e9, 3)}),
+              flush=True)
         return
 
     cfg = CONFIGS[args.config]
