@@ -135,30 +135,38 @@ __device__ __forceinline__ bf16x8 lds_read_tr(const char* base, int off0, int of
 // the main kernel's accumulators start from: -Dl, and -lse/scale (rows past
 // S: 0 and -inf, so that P = 0 there).
 __global__ __launch_bounds__(256) void bwd_preprocess(PreParams p) {
+  // Rows are taken in the memory order of o and dout ([B, S, Hq, D]: the
+  // rows of one block are contiguous), then the padding rows past S; each
+  // row's value is stored at its [B*Hq][NT] position.  (Row counts fit in 32
+  // bits: the host refuses sizes whose element offsets do not.)
   const int lpr = p.D / 8;
   const int rows_per_block = 256 / lpr;
-  const long long row = (long long)blockIdx.x * rows_per_block + threadIdx.x / lpr;
+  const int row = blockIdx.x * rows_per_block + threadIdx.x / lpr;
   const int sub = threadIdx.x % lpr;
-  const long long nrows = (long long)p.B * p.Hq * p.NT;
+  const int real = p.B * p.S * p.Hq;
+  const int nrows = p.B * p.Hq * p.NT;
   float acc = 0.0f;
-  long long bh = 0;
-  int s = 0;
-  if (row < nrows) {
-    bh = row / p.NT;
-    s = (int)(row - bh * p.NT);
-    if (s < p.S) {
-      const long long b = bh / p.Hq, h = bh - b * p.Hq;
-      const size_t off = ((size_t)(b * p.S + s) * p.Hq + h) * p.D + 8 * sub;
-      const bf16x8 o = *reinterpret_cast<const bf16x8*>((const bf16*)p.o + off);
-      const bf16x8 g = *reinterpret_cast<const bf16x8*>((const bf16*)p.dout + off);
+  int bh = 0, s = 0;
+  if (row < real) {
+    const int bs = row / p.Hq, h = row - bs * p.Hq;
+    const int b = bs / p.S;
+    s = bs - b * p.S;
+    bh = b * p.Hq + h;
+    const size_t off = (size_t)row * p.D + 8 * sub;
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>((const bf16*)p.o + off);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>((const bf16*)p.dout + off);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)g[e];
-    }
+    for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)g[e];
+  } else if (row < nrows) {
+    const int pad = p.NT - p.S, pr = row - real;
+    bh = pr / pad;
+    s = p.S + (pr - bh * pad);
   }
   for (int m = lpr / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (row < nrows && sub == 0) {
-    p.delta[row] = -acc;
-    p.lse2[row] = s < p.S ? -p.lse[bh * p.S + s] * p.inv_scale : -__builtin_inff();
+    const long long drow = (long long)bh * p.NT + s;
+    p.delta[drow] = -acc;
+    p.lse2[drow] = s < p.S ? -p.lse[(long long)bh * p.S + s] * p.inv_scale : -__builtin_inff();
   }
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long nthreads = (long long)gridDim.x * blockDim.x;
