@@ -549,13 +549,13 @@ __device__ __forceinline__ void acquire(const int* cnt, int expect, int polled, 
 //   * slice `prev` (the previous pass): its turn, polled at the start of the
 //     pass, is checked at the end, then its partial sum is loaded into dq_ld
 //     for the next pass (zeros when there is nothing to add).
-// The loads thus have a whole pass to arrive, and the stores a whole pass to
-// complete before the counter is bumped after the next barrier.  Everything
-// from the first product to the last dS write has no branches, so that the
-// compiler can interleave the softmax with the dQ and dV/dK products (without
-// a slice two passes back the dQ product is formed and dropped).  Writes dS
-// of this pass into lS_cur.  When masked, elements with their bit set in zb[m]
-// start at -inf (P = 0).
+// The partial-sum loads thus have most of a pass to arrive; the stores are
+// acknowledged at the wait at the top of the next pass, after which the
+// counter is bumped.  Everything from the first product to the dQ product has
+// no branches, and scheduling barriers fix how far ahead of their products
+// the fragment reads are issued (without a slice two passes back the dQ
+// product is formed and dropped).  Writes dS of this pass into lS_cur.  When
+// masked, elements with their bit set in zb[m] start at -inf (P = 0).
 template <int D, int T, bool CAUSAL, bool ATOMIC>
 __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const char* lL, char* lS_cur,
                                           const char* lS_ld, const LaneOffs<D, T>& o, int qg, int hg, int lane,
@@ -620,7 +620,7 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
     }
   }
 
-  // ---- dQ of the slice two passes back, next to the softmax
+  // ---- softmax: P and dS of this pass in bf16
   bf16x8 pb[QBP][2], dsb[QBP][2];
 #pragma unroll
   for (int m = 0; m < QBP; ++m) softmax_block(sa[m], pa[m], scale_log2e, pb[m], dsb[m]);
