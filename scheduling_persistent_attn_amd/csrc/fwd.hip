@@ -9,7 +9,10 @@
 //   row statistics are lane-local plus one exchange with lane ^ 32
 //   O^T += V^T P^T         A = V^T (LDS, transposed), B = P^T (registers, the
 //                          accumulator layout reused as the B operand)
-// exp is computed as exp2 with the scale folded into log2(e).
+// exp is computed as exp2 with the scale folded into log2(e).  Two workgroups
+// per compute unit (the register budget is capped at two waves per SIMD), so
+// one workgroup's loads overlap the other's products; with a causal mask the
+// query blocks with the most key blocks are launched first.
 
 #include <hip/hip_runtime.h>
 
@@ -42,7 +45,7 @@ __device__ __forceinline__ int tr_off_f(int d, int v) {
 }  // namespace
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(FwdParams p) {
   constexpr int BQ = 128, BK = 64;
   constexpr int KBD = D / 16, DB = D / 32, CHD = D / 8, C8 = BK / 4;
   __shared__ __attribute__((aligned(16))) bf16 sK[BK * D];
@@ -50,7 +53,10 @@ __global__ __launch_bounds__(256) void attn_fwd(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, c = lane & 31, hg = lane >> 5;
-  const int qblk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // causal: the query blocks with the most key blocks first (the grid's
+  // tail is then made of short blocks)
+  const int qblk = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int hk = h / p.G;
   const int S = p.S;
   const bf16* gq = (const bf16*)p.q;
