@@ -136,6 +136,25 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
             "wall_ms_per_step": 1e3 * wall / steps}
 
 
+def time_forward(dash, x, cfg, steps, warmup):
+    """Mean event-timed duration of dash_attn_fwd (O and LSE) on this input,
+    outputs allocated once outside the timed region."""
+    import torch
+    o, lse = dash.forward(x["q"], x["k"], x["v"], cfg["causal"])
+    mask = dash.MASK_CAUSAL if cfg["causal"] else dash.MASK_FULL
+    for _ in range(warmup):
+        dash.dash_attn_fwd(x["q"], x["k"], x["v"], o, lse, mask)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dash.dash_attn_fwd(x["q"], x["k"], x["v"], o, lse, mask)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def committed_traffic(config, schedule):
     """Calibrated HBM bytes per launch of the persistent kernel, from the
     committed rocprofv3 summary; None if there is none or it was taken on a
@@ -307,6 +326,14 @@ def main():
         "roofline": roofline(cfg, T, fl, bestr["kernel_ms_mean"], best,
                              committed_traffic(args.config, best)),
     }
+    # the whole attention layer: forward (O, LSE) then the backward step
+    # above; forward FLOPs are 4*B*Hq*S^2*D (halved for a causal mask)
+    fwd_ms = time_forward(dash, x, cfg, args.steps, args.warmup)
+    layer_ms = fwd_ms + bestr["ms_mean"]
+    line["layer"] = {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bestr["ms_mean"], 4),
+                     "ms": round(layer_ms, 4),
+                     "tflops": round(1.4 * fl / (layer_ms * 1e-3) / 1e12, 3),
+                     "fwd_tflops": round(0.4 * fl / (fwd_ms * 1e-3) / 1e12, 3)}
     # the schedule the simulator picks for this shape on this device (AUTO)
     names = {v: k for k, v in dash.SCHEDULES.items()}
     auto = names[dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, 1 if cfg["causal"] else 0)]
