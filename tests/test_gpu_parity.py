@@ -74,6 +74,30 @@ def test_forward_parity(case):
     assert e_l[2] <= 1e-3
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_parity_growing_scores(causal, D):
+    """Key magnitudes that grow along the sequence: later 64-key blocks raise
+    the row maxima by many units of log2, so the forward moves its running
+    reference point several times (rescaling O and the row sums), and in
+    between the unnormalised probabilities exceed 1."""
+    B, S, Hq, Hkv = 1, 520, 2, 1
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D)
+    ramp = torch.linspace(0.25, 4.0, S, dtype=torch.float32).view(1, S, 1, 1)
+    x = dict(x, k=(x["k"].float().cpu() * ramp).to(torch.bfloat16).cuda())
+    h = {k: gu.host64(v) for k, v in x.items()}
+    o_ref, lse_ref = oa.attention_forward(h["q"], h["k"], h["v"], causal)
+    print("forward growing scores", causal, D, flush=True)
+    o, lse = gu.run_forward(x, causal)
+    torch.cuda.synchronize()
+    e_o = gu.errors(gu.host64(o), o_ref)
+    e_l = gu.errors(lse.double().cpu().numpy(), lse_ref)
+    print("  O rel-l2 %.3e max-abs(excess) %.3e max-abs %.3e | LSE rel-l2 %.3e max-abs %.3e"
+          % (e_o + (e_l[0], e_l[2])))
+    assert gu.within(e_o)
+    assert e_l[2] <= 1e-3 * max(1.0, float(np.max(np.abs(lse_ref))))
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dS%dH%d-%dD%d%s" % (
     c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "f"))
 def test_backward_parity_all_schedules(case):
