@@ -118,7 +118,9 @@ size_t dash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int S, int D,
 /* Attention forward (support for the backward): o = softmax(scale*q k^T +
  * mask) v in bf16 (round to nearest even) and lse in fp32.  Overwrites o and
  * lse.  Not part of the deterministic-reduction contract, but itself
- * deterministic (no cross-workgroup reduction). */
+ * deterministic (no cross-workgroup reduction).  Layouts, alignment and the
+ * shape errors are those of dash_attn_bwd; DASH_ERR_UNSUPPORTED also when
+ * B*S*Hq*D >= 2^31 (the kernel forms 32-bit offsets) or B > 65535. */
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o,
                   float* lse, int B, int Hq, int Hkv, int S, int D, int mask,
                   void* stream);

@@ -205,6 +205,8 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   int Hq, int Hkv, int S, int D, int mask, void* stream) {
   int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_NAIVE);
   if (st != DASH_OK) return st;
+  // 32-bit element offsets inside the kernel; the batch is a grid dimension
+  if ((long long)B * S * Hq * D >= (1LL << 31) || B > 65535) return DASH_ERR_UNSUPPORTED;
   if (B == 0 || S == 0) return DASH_OK;
   if (!q || !k || !v || !o || !lse) return DASH_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||

@@ -1,7 +1,7 @@
 // Attention forward for gfx950: produces O (bf16) and the natural-log LSE
 // (fp32) that the backward consumes.  Not part of the scheduled backward; one
-// workgroup per (128-row query block, query head, batch), no cross-workgroup
-// reduction, hence deterministic.
+// workgroup of 8 waves per (256-row query block, query head, batch), no
+// cross-workgroup reduction, hence deterministic.
 //
 // Wave w owns query rows [32w, 32w+32) of the block.  Per 64-key block:
 //   S^T  = K Q^T           A = K rows (LDS, 16-byte reads), B = Q fragments
@@ -15,10 +15,11 @@
 // flight while the current block's products run.  exp is computed as exp2
 // with the scale folded into one FMA; the mask is applied only on blocks that
 // cross the diagonal or the end of the sequence; O is rescaled only when a
-// row maximum outgrows the running reference point by more than 2^8.  Two
-// workgroups per compute unit (the register budget is capped at two waves per
-// SIMD); with a causal mask the query blocks with the most key blocks are
-// launched first.
+// row maximum outgrows the running reference point by more than 2^8.  One
+// workgroup per compute unit (two waves per SIMD, the register budget capped
+// to match), so each key/value block staged in LDS serves 256 query rows;
+// with a causal mask the query blocks with the most key blocks are launched
+// first.
 
 #include <hip/hip_runtime.h>
 
@@ -42,10 +43,10 @@ __device__ __forceinline__ f32x16 mfma_f(bf16x8 a, bf16x8 b, f32x16 c) {
 }  // namespace
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(FwdParams p) {
-  constexpr int BQ = 128, BK = 64, RB = 2 * D;  // RB: bytes of one K or V row
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(FwdParams p) {
+  constexpr int BQ = 256, NT = 512, BK = 64, RB = 2 * D;  // RB: bytes of one K or V row
   constexpr int KBD = D / 16, DB = D / 32, CHD = D / 8;
-  constexpr int NLD = BK * CHD / 256;           // 16-byte chunks per thread per tile
+  constexpr int NLD = BK * CHD / NT;            // 16-byte chunks per thread per tile
   constexpr float kGrow = 8.0f;                 // log2 headroom before O is rescaled
   __shared__ __attribute__((aligned(16))) char sK[BK * RB];
   __shared__ __attribute__((aligned(16))) char sV[BK * RB];
@@ -54,10 +55,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63, c = lane & 31, hg = lane >> 5;
   const int g16 = lane >> 4, s16 = lane & 15;
-  // causal: the query blocks with the most key blocks first (the grid's
-  // tail is then made of short blocks)
-  const int qblk = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dispatched in linear order.  Causal: grid (Hq, B, blocks),
+  // the query blocks with the most key blocks first across all heads, so the
+  // grid's tail is made of short blocks.  Full mask: grid (blocks, Hq, B), so
+  // the workgroups in flight share the keys and values of a few heads.
+  const int qblk = CAUSAL ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.x;
+  const int h = CAUSAL ? blockIdx.x : blockIdx.y, b = CAUSAL ? blockIdx.y : blockIdx.z;
   const int hk = h / p.G;
   const int S = p.S;
   const float c2 = p.scale_log2e;
@@ -86,12 +89,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int col = 16 * (g16 & 1) + 4 * (s16 & 3);
     offT[h8] = lds_phys<RB>(8 * h8 + 4 * hg + (s16 >> 2), col >> 3) + 2 * (col & 7);
   }
-  // loader: chunk tid + 256e of a tile is row tid / CHD + e * 256 / CHD,
+  // loader: chunk tid + NT e of a tile is row tid / CHD + e NT / CHD,
   // chunk tid % CHD.  Loads go through a buffer resource that ends at the
   // last key of the sequence, so rows past it read as zero.
   int ldo[NLD];
 #pragma unroll
-  for (int e = 0; e < NLD; ++e) ldo[e] = lds_phys<RB>((tid + 256 * e) / CHD, tid % CHD);
+  for (int e = 0; e < NLD; ++e) ldo[e] = lds_phys<RB>((tid + NT * e) / CHD, tid % CHD);
   const int krs = p.Hkv * D;                                     // key stride (elements)
   const int voff = ((tid / CHD) * krs + 8 * (tid % CHD)) * 2;   // bytes
   const size_t head0 = ((size_t)b * S * p.Hkv + hk) * D;         // key 0 of this head
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         (void*)(gv + head0 + (size_t)k0 * krs), 0, nbytes, 0x00020000);
 #pragma unroll
     for (int e = 0; e < NLD; ++e) {
-      const int soff = e * (256 / CHD) * krs * 2;
+      const int soff = e * (NT / CHD) * krs * 2;
       kr[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, soff, 0));
       vr[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, soff, 0));
     }
@@ -237,14 +240,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 hipError_t launch_fwd(int D, bool causal, const FwdParams& p, hipStream_t s) {
-  const dim3 grid((p.S + 127) / 128, p.Hq, p.B);
+  const int nq = (p.S + 255) / 256;  // 256-row query blocks
+  const dim3 grid = causal ? dim3(p.Hq, p.B, nq) : dim3(nq, p.Hq, p.B);
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   if (D == 64) {
-    if (causal) hipLaunchKernelGGL((attn_fwd<64, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd<64, false>), grid, dim3(256), 0, s, p);
+    if (causal) hipLaunchKernelGGL((attn_fwd<64, true>), grid, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd<64, false>), grid, dim3(512), 0, s, p);
   } else if (D == 128) {
-    if (causal) hipLaunchKernelGGL((attn_fwd<128, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd<128, false>), grid, dim3(256), 0, s, p);
+    if (causal) hipLaunchKernelGGL((attn_fwd<128, true>), grid, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd<128, false>), grid, dim3(512), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

@@ -106,6 +106,9 @@ def test_fwd_validation_before_device():
     assert f(a, a, a, a, a, 1, 2, 2, 256, 72, 0, None) == dash.DASH_ERR_UNSUPPORTED
     assert f(a, a, a, a, a, 1, 2, 2, 256, 64, 5, None) == dash.DASH_ERR_SCHEDULE_MASK
     assert f(None, None, None, None, None, 1, 2, 2, 0, 64, 0, None) == dash.DASH_OK
+    # 32-bit element offsets and the batch grid dimension bound the problem
+    assert f(a, a, a, a, a, 1, 128, 8, 1 << 17, 128, 1, None) == dash.DASH_ERR_UNSUPPORTED
+    assert f(a, a, a, a, a, 65536, 1, 1, 1, 64, 0, None) == dash.DASH_ERR_UNSUPPORTED
 
 
 COMBOS = [(s, m) for s in (sch.NAIVE, sch.DESCENDING_Q, sch.SHIFT, sch.ATOMIC)
