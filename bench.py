@@ -232,6 +232,36 @@ def roofline(cfg, T, fl, kernel_ms, schedule, traffic):
     return r
 
 
+def sim_report():
+    """Critical path, efficiency and Lemma 1 check of every schedule on every
+    large workload, from the library's simulator: P = 256 workers (the
+    compute units of an MI355X) and 132 (the SM count of the H800 the pages
+    measure on), dynamic dispatch, c = c_diag = 1, r/c in {0, 0.1, 0.25}.
+    One line of JSON per case."""
+    import scheduling_persistent_attn_amd as dash
+    names = {v: k for k, v in dash.SCHEDULES.items()}
+    for name in ("llama8b_causal", "dit_full", "long_full", "qwen7b_causal"):
+        cfg = CONFIGS[name]
+        T = dash.dash_attn_tile_size(cfg["S"], cfg["D"])
+        N = (cfg["S"] + T - 1) // T
+        G = cfg["Hq"] // cfg["Hkv"]
+        groups = cfg["B"] * cfg["Hkv"]
+        mask = 1 if cfg["causal"] else 0
+        for P in (256, 132):
+            for r in (0.0, 0.1, 0.25):
+                for sched in (dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT, dash.SYMMETRIC_SHIFT):
+                    if sched == dash.SYMMETRIC_SHIFT and (not mask or N % 2):
+                        continue
+                    res = dash.dash_sim_run(mask, sched, N, G, groups, P, 1, 1.0, 1.0, r)
+                    print(json.dumps({"workload": name, "N": N, "G": G, "groups": groups,
+                                      "P": P, "r_over_c": r, "schedule": names[sched],
+                                      "critical_path": res["makespan"],
+                                      "efficiency": res["efficiency"],
+                                      "lemma1_violations": res["violations"],
+                                      "order_edges": res["order_edges"],
+                                      "deadlock": bool(res["deadlock"])}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,7 +274,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--sim-report", action="store_true",
+                    help="only print the schedule simulator's critical paths for every "
+                         "workload and schedule (CPU; no GPU needed)")
     args = ap.parse_args()
+    if args.sim_report:
+        sim_report()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

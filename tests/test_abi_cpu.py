@@ -10,6 +10,7 @@
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 
@@ -272,3 +273,25 @@ def test_auto_schedule_arguments():
     assert _bwd(sched=dash.AUTO, q=None) == dash.DASH_ERR_NULL
     assert _bwd(sched=dash.AUTO, ws=None) == dash.DASH_ERR_WORKSPACE
     assert _bwd(sched=dash.AUTO, S=0, q=None, ws=None) == dash.DASH_OK
+
+
+def test_sim_report_closed_forms(capsys):
+    """bench.py --sim-report on the large workloads; two cases have closed
+    forms.  dit_full at P = 256, r = 0: 48 groups x 32 chains of 32 unit tasks
+    on 256 workers are 6 rounds of 32, so every schedule's critical path is 192.
+    llama8b_causal, symmetric shift, P = 256, r = 0: 32 groups x 16 pairs of
+    33 tasks for each of 4 query heads (132 per item) in 2 rounds: 264, with
+    efficiency 1 and no Lemma 1 violation."""
+    import json
+    sys.path.insert(0, str(ROOT))
+    import bench
+    bench.sim_report()
+    rows = [json.loads(l) for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
+    assert len(rows) == 84
+    pick = {(r["workload"], r["P"], r["r_over_c"], r["schedule"]): r for r in rows}
+    for s in ("naive", "descending_q", "shift"):
+        assert pick[("dit_full", 256, 0.0, s)]["critical_path"] == 192.0
+    sym = pick[("llama8b_causal", 256, 0.0, "symmetric_shift")]
+    assert sym["critical_path"] == 264.0 and sym["lemma1_violations"] == 0
+    assert abs(sym["efficiency"] - 1.0) < 1e-12
+    assert not any(r["deadlock"] for r in rows)
