@@ -173,8 +173,10 @@ def committed_traffic(config, schedule):
 
 
 def cpu_baseline(cfg, budget_s=20.0):
-    """Time the float64 oracle on whole (batch 0, kv head) groups until the
-    budget is used; report the rate in TFLOP/s of the same FLOP formula."""
+    """Time the float64 oracle on whole (batch, kv head) groups of the
+    workload until the budget is used or every group is done; report the
+    rate in TFLOP/s of the same FLOP formula.  Batch 0's inputs stand in for
+    every batch (the oracle's work does not depend on the values)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import attention as oa
@@ -192,7 +194,7 @@ def cpu_baseline(cfg, budget_s=20.0):
         oa.attention_backward(h["q"][:, :, hs], h["k"][:, :, kv:kv + 1],
                               h["v"][:, :, kv:kv + 1], h["do"][:, :, hs], cfg["causal"])
         groups += 1
-        if time.perf_counter() - t0 >= budget_s or groups >= Hkv:
+        if time.perf_counter() - t0 >= budget_s or groups >= B * Hkv:
             break
     dt = time.perf_counter() - t0
     fl = flops(dict(cfg, B=1, Hq=G * groups))
@@ -203,8 +205,9 @@ def cpu_baseline(cfg, budget_s=20.0):
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
             "sample": "float64 oracle forward+backward of %d of %d (batch, kv head) groups "
-                      "(%d query heads, batch 0) at S=%d D=%d, %.1f s; includes the oracle's "
-                      "own float64 forward" % (groups, B * Hkv, G * groups, S, D, dt)}
+                      "(%d query heads; batch 0's inputs for every batch) at S=%d D=%d, %.1f s; "
+                      "includes the oracle's own float64 forward"
+                      % (groups, B * Hkv, G * groups, S, D, dt)}
 
 
 def roofline(cfg, T, fl, kernel_ms, schedule, traffic):
