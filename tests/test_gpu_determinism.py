@@ -28,6 +28,7 @@ CASES = [
     (1, 1024, 8, 2, 128, True),
     (2, 1024, 4, 4, 64, False),
     (1, 2048, 8, 8, 128, False),
+    (2, 1024, 16, 4, 128, True),  # 8 groups: one item queue per XCD
 ]
 
 

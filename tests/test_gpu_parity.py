@@ -32,6 +32,8 @@ CASES = [
     (1, 1024, 2, 1, 64, True),    # D = 64 with 128 tiles, N = 8
     (1, 1, 2, 1, 64, True),       # single token
     (1, 64, 1, 1, 128, False),    # single partial tile
+    (2, 512, 8, 4, 64, True),     # 8 (batch, kv head) groups: one item queue per XCD
+    (2, 512, 8, 4, 128, False),
 ]
 
 
