@@ -174,6 +174,16 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v,
  * error, else DASH_OK.  Reads 8 bytes of the workspace. */
 int dash_attn_bwd_check(const void* workspace, void* stream);
 
+/* Sets the device watchdog of the ordered reductions for the backward calls
+ * planned after it, process-wide: a wave that has waited `seconds` of wall
+ * clock for its turn gives up and raises the workspace's error flag; every
+ * later wait of that launch then gives up within 64 polls, so the launch
+ * drains and dash_attn_bwd_check reports DASH_ERR_TIMEOUT.  The default is
+ * 2 s.  0 makes any wait longer than 64 polls time out (a caller can force
+ * the error path this way).  Returns DASH_ERR_SHAPE, leaving the setting
+ * unchanged, for a negative or non-finite value or one above 3600 s. */
+int dash_attn_set_watchdog(double seconds);
+
 /* The deterministic schedule that DASH_SCHED_AUTO resolves to for these
  * arguments on the current device, or minus a dash_status.  The choice is
  * dash_sim_select over the device's persistent grid (P = the workgroups

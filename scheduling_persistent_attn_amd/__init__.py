@@ -32,7 +32,7 @@ SYMBOLS = (
     "dash_attn_bwd", "dash_attn_bwd_prepare", "dash_attn_bwd_run", "dash_attn_bwd_check", "dash_status_string",
     "dash_attn_bwd_grid_size", "dash_schedule_num_items",
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
-    "dash_attn_bwd_auto_schedule",
+    "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog",
 )
 
 
@@ -79,6 +79,8 @@ def lib():
     L.dash_attn_bwd_run.restype = i
     L.dash_attn_bwd_check.argtypes = [p, p]
     L.dash_attn_bwd_check.restype = i
+    L.dash_attn_set_watchdog.argtypes = [d]
+    L.dash_attn_set_watchdog.restype = i
     L.dash_status_string.argtypes = [i]
     L.dash_status_string.restype = ctypes.c_char_p
     L.dash_attn_bwd_grid_size.argtypes = [i, i, i]
@@ -261,6 +263,12 @@ def dash_attn_bwd_check(workspace, stream=None):
     st = lib().dash_attn_bwd_check(_ptr(workspace), _stream(stream))
     if st != DASH_OK:
         raise DashError(st, "dash_attn_bwd_check")
+
+
+def dash_attn_set_watchdog(seconds):
+    st = lib().dash_attn_set_watchdog(float(seconds))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_set_watchdog")
 
 
 # --- conveniences that allocate outputs with torch --------------------------

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -14,7 +15,9 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr double kWatchdogSeconds = 2.0;
+
+// wall-clock limit of one turn wait, in microseconds (dash_attn_set_watchdog)
+std::atomic<long long> g_watchdog_us{2000000};
 
 struct DeviceInfo {
   bool ready = false;
@@ -333,7 +336,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   bp.total_items = B * Hkv * ipg;
   bp.scale = (float)(1.0 / __builtin_sqrt((double)D));
   bp.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
-  bp.spin_ticks = (long long)(kWatchdogSeconds * 1000.0 * (double)dev->wall_khz);
+  bp.spin_ticks = g_watchdog_us.load() * dev->wall_khz / 1000;
   P->grid = grid < bp.total_items ? grid : bp.total_items;
 
   dash::FinParams& fp = P->fp;
@@ -405,6 +408,12 @@ int dash_attn_bwd_check(const void* workspace, void* stream) {
       hipSuccess)
     return DASH_ERR_HIP;
   return flag[0] ? DASH_ERR_TIMEOUT : DASH_OK;
+}
+
+int dash_attn_set_watchdog(double seconds) {
+  if (!(seconds >= 0.0 && seconds <= 3600.0)) return DASH_ERR_SHAPE;  // also NaN
+  g_watchdog_us.store((long long)(seconds * 1e6));
+  return DASH_OK;
 }
 
 int dash_schedule_num_items(int mask, int schedule, int N) {

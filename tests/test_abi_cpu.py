@@ -37,6 +37,17 @@ def test_header_symbols_exported():
     assert set(names) == set(dash.SYMBOLS)
 
 
+def test_watchdog_setting_validation():
+    # out-of-range limits are refused and leave the setting alone; the
+    # setter touches no device
+    for bad in (-1.0, float("nan"), float("inf"), 3600.5):
+        with pytest.raises(dash.DashError) as e:
+            dash.dash_attn_set_watchdog(bad)
+        assert e.value.status == dash.DASH_ERR_SHAPE
+    for ok in (0.0, 1e-6, 3600.0, 2.0):
+        dash.dash_attn_set_watchdog(ok)
+
+
 def test_status_strings():
     for s in range(8):
         assert dash.dash_status_string(s)

@@ -1,0 +1,56 @@
+"""The watchdog error path of the ordered reduction, forced from the host.
+
+With a zero wall-clock limit any turn wait longer than 64 polls gives up.  The
+naive (rigid ascending) order on a causal mask with 32 tiles makes chain i
+wait about i task-times for its first turn, so some wait does; the kernel then
+raises the workspace flag, every later wait gives up at once, the launch
+drains, and dash_attn_bwd_check reports DASH_ERR_TIMEOUT.  With the default
+limit restored, the next call on the same workspace is bit-identical to a run
+before the forced failure (the preprocess clears the flag).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import scheduling_persistent_attn_amd as dash
+
+sys.path.insert(0, __file__.rsplit("/", 1)[0])
+import gpu_util as gu  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+CASE = (1, 4096, 8, 8, 128, True)  # B, S, Hq, Hkv, D, causal: N = 32
+
+
+def _bits(ts):
+    return [t.view(torch.int16).cpu().numpy().copy() for t in ts]
+
+
+def test_forced_timeout_is_reported_and_recovers():
+    B, S, Hq, Hkv, D, causal = CASE
+    print("watchdog", CASE, "naive", flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=2300)
+    o, lse = gu.run_forward(x, causal)
+    ws = dash.new_workspace(x["q"], x["k"], int(causal), dash.NAIVE)
+    good = _bits(gu.run_backward(x, o, lse, causal, dash.NAIVE, workspace=ws))
+    dash.dash_attn_bwd_check(ws)
+    try:
+        dash.dash_attn_set_watchdog(0.0)
+        gu.run_backward(x, o, lse, causal, dash.NAIVE, workspace=ws)
+        with pytest.raises(dash.DashError) as e:
+            dash.dash_attn_bwd_check(ws)
+        assert e.value.status == dash.DASH_ERR_TIMEOUT
+        ctrl = ws.view(torch.int32)[:3].cpu().numpy()
+        print("flag %d, waits that timed out %d" % (ctrl[1], ctrl[2]), flush=True)
+        assert ctrl[1] == 1 and ctrl[2] >= 1
+    finally:
+        dash.dash_attn_set_watchdog(2.0)
+    again = _bits(gu.run_backward(x, o, lse, causal, dash.NAIVE, workspace=ws))
+    dash.dash_attn_bwd_check(ws)
+    for a, b in zip(good, again):
+        assert np.array_equal(a, b)
+    cnt = gu.read_counters(ws, B, Hq, S, D)
+    assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
