@@ -8,7 +8,10 @@ for the atomic reference the finalize pass) over one batch of synthetic bf16
 input already resident in HBM.  Each schedule is timed separately: W untimed
 steps, then K steps between two device synchronisations, with HIP events
 recorded on the call's stream before the preprocess, between the phases and
-after the persistent kernel.  Prints one JSON line.
+after the persistent kernel.  Prints one JSON line.  Outside the timed
+region each schedule's output is checked for run-to-run bit identity at this
+size (the first warm-up output against the last timed step and five more
+steps on rotating streams behind a random amount of unrelated work).
 
 The headline value is the whole-step throughput of the fastest deterministic
 schedule in TFLOP/s with FLOPs = 10*B*Hq*S^2*D (halved for a causal mask).  The
@@ -105,20 +108,26 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
     # events on the stream the kernels are launched on
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
 
-    def step(e=None):
+    def step(e=None, s=None):
+        s = stream if s is None else s
         if e:
-            e[0].record(stream)
+            e[0].record(s)
         dash.dash_attn_bwd_prepare(o, x["do"], lse, tuple(x["q"].shape), Hkv, mask, sched,
-                                   ws, stream)
+                                   ws, s)
         if e:
-            e[1].record(stream)
+            e[1].record(s)
         dash.dash_attn_bwd_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, mask, sched,
-                               ws, stream)
+                               ws, s)
         if e:
-            e[2].record(stream)
+            e[2].record(s)
 
-    for _ in range(warmup):
+    def bits():
+        return [t.view(torch.int16).clone() for t in (dq, dk, dv)]
+
+    for n in range(warmup):
         step()
+        if n == 0:
+            ref = bits()  # the reference for the run-to-run check below
     dash.dash_attn_bwd_check(ws, stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -129,11 +138,39 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
     dash.dash_attn_bwd_check(ws, stream)
     per = sorted(e[0].elapsed_time(e[2]) for e in ev)
     kern = [e[1].elapsed_time(e[2]) for e in ev]
-    return {"ms_mean": sum(per) / len(per), "ms_median": per[len(per) // 2],
-            "ms_p10": per[len(per) // 10],
-            "ms_p90": per[min(len(per) - 1, (9 * len(per)) // 10)],
-            "kernel_ms_mean": sum(kern) / len(kern),
-            "wall_ms_per_step": 1e3 * wall / steps}
+    out = {"ms_mean": sum(per) / len(per), "ms_median": per[len(per) // 2],
+           "ms_p10": per[len(per) // 10],
+           "ms_p90": per[min(len(per) - 1, (9 * len(per)) // 10)],
+           "kernel_ms_mean": sum(kern) / len(kern),
+           "wall_ms_per_step": 1e3 * wall / steps}
+    if warmup > 0:
+        out["repro"] = reproducibility(dash, step, bits, ref, ws)
+    return out
+
+
+def reproducibility(dash, step, bits, ref, ws, extra=5):
+    """Outside the timed region: the outputs of the last timed step and of
+    `extra` more steps, each on one of three streams behind a seeded random
+    amount of unrelated work, compared bit for bit with the first warm-up
+    step's.  Returns the number of runs compared and how many differed."""
+    import random
+    import torch
+    differ = int(any(not torch.equal(a, b) for a, b in zip(ref, bits())))
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    filler = torch.ones(1 << 22, device=ref[0].device)
+    rng = random.Random(1234)
+    for n in range(extra):
+        s = streams[n % 3]
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(rng.randint(0, 6)):
+                filler.mul_(1.0001)
+            step(s=s)
+            dash.dash_attn_bwd_check(ws, s)
+            differ += int(any(not torch.equal(a, b) for a, b in zip(ref, bits())))
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return {"runs": extra + 1, "differ": differ}
 
 
 def time_forward(dash, x, cfg, steps, warmup):
@@ -333,8 +370,10 @@ def main():
         r["kernel_tflops"] = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
         r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
         results[name] = r
-        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak  (kernel %.3f ms)"
-            % (name, r["ms_mean"], r["tflops"], r["pct_peak"], r["kernel_ms_mean"]))
+        rep = r.get("repro")
+        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak  (kernel %.3f ms)%s"
+            % (name, r["ms_mean"], r["tflops"], r["pct_peak"], r["kernel_ms_mean"],
+               "  %d of %d runs differ from the first" % (rep["differ"], rep["runs"]) if rep else ""))
     det = {k: v for k, v in results.items() if k != "atomic"}
     best = max(det, key=lambda k: det[k]["tflops"])
     atomic = results.get("atomic")
@@ -365,6 +404,11 @@ def main():
         "roofline": roofline(cfg, T, fl, bestr["kernel_ms_mean"], best,
                              committed_traffic(args.config, best)),
     }
+    # run-to-run bit identity at this size, in this launch configuration:
+    # every deterministic schedule must reproduce its first output exactly
+    # (the atomic reference's count of differing runs is the positive control)
+    if all("repro" in v for v in det.values()):
+        line["deterministic_bit_identical"] = all(v["repro"]["differ"] == 0 for v in det.values())
     # the whole attention layer: forward (O, LSE) then the backward step
     # above; forward FLOPs are 4*B*Hq*S^2*D (halved for a causal mask)
     fwd_ms = time_forward(dash, x, cfg, args.steps, args.warmup)
