@@ -148,3 +148,22 @@ def test_symmetric_rejects_odd_tile_count():
         gu.run_backward(x, o, lse, True, dash.SYMMETRIC_SHIFT,
                         workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
     assert e.value.status == dash.DASH_ERR_SCHEDULE_MASK
+
+
+
+def test_shift_rejects_groups_larger_than_the_grid():
+    # a (batch, kv head) group of shift items (one per key/value tile) must be
+    # resident at once: with one tile more than the device runs workgroups the
+    # call is refused on the host, before anything is enqueued
+    D = 128
+    T = dash.dash_attn_tile_size(4096, D)
+    for causal in (False, True):
+        grid = dash.dash_attn_bwd_grid_size(4096, D, int(causal))
+        S = (grid + 1) * T
+        print("residency", causal, grid, S, flush=True)
+        x = gu.gpu_inputs(1, S, 1, 1, D)
+        o, lse = gu.run_forward(x, causal)
+        ws = dash.new_workspace(x["q"], x["k"], int(causal), dash.SHIFT)
+        with pytest.raises(dash.DashError) as e:
+            gu.run_backward(x, o, lse, causal, dash.SHIFT, workspace=ws)
+        assert e.value.status == dash.DASH_ERR_UNSUPPORTED
