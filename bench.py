@@ -11,7 +11,10 @@ recorded on the call's stream before the preprocess, between the phases and
 after the persistent kernel.  Prints one JSON line.  Outside the timed
 region each schedule's output is checked for run-to-run bit identity at this
 size (the first warm-up output against the last timed step and five more
-steps on rotating streams behind a random amount of unrelated work).
+steps on rotating streams behind a random amount of unrelated work), and the
+last timed step's turn waits are read from the workspace: `wait_fraction` is
+the time waves spent waiting for an earlier dQ contribution, as a share of
+the persistent grid's wave time (the schedule's bubbles).
 
 The headline value is the whole-step throughput of the fastest deterministic
 schedule in TFLOP/s with FLOPs = 10*B*Hq*S^2*D (halved for a causal mask).  The
@@ -143,6 +146,13 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
            "ms_p90": per[min(len(per) - 1, (9 * len(per)) // 10)],
            "kernel_ms_mean": sum(kern) / len(kern),
            "wall_ms_per_step": 1e3 * wall / steps}
+    # the last timed step's bubbles: time its waves spent waiting for a turn,
+    # as a share of the time all waves of the persistent grid were resident
+    wst = dash.dash_attn_bwd_wait_stats(ws, stream)
+    S, D = x["q"].shape[1], x["q"].shape[3]
+    waves = dash.dash_attn_bwd_grid_size(S, D, mask) * dash.dash_attn_tile_size(S, D) // 32
+    out["turn_waits"] = wst["waits"]
+    out["wait_fraction"] = wst["wait_seconds"] / (waves * kern[-1] * 1e-3)
     if warmup > 0:
         out["repro"] = reproducibility(dash, step, bits, ref, ws)
     return out
@@ -371,8 +381,9 @@ def main():
         r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
         results[name] = r
         rep = r.get("repro")
-        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak  (kernel %.3f ms)%s"
+        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak  (kernel %.3f ms)  waiting %4.1f%%%s"
             % (name, r["ms_mean"], r["tflops"], r["pct_peak"], r["kernel_ms_mean"],
+               100.0 * r["wait_fraction"],
                "  %d of %d runs differ from the first" % (rep["differ"], rep["runs"]) if rep else ""))
     det = {k: v for k, v in results.items() if k != "atomic"}
     best = max(det, key=lambda k: det[k]["tflops"])

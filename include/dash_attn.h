@@ -103,6 +103,10 @@ int dash_attn_tile_size(int S, int D);
  * arguments are invalid.  Layout (offsets rounded up to 256 bytes):
  *   ctrl      64 x int32   [0] work-dispatch counter, [1] watchdog flag,
  *                          [2] number of waits that timed out
+ *   waits     4096 x 4 uint64: per wave of the persistent grid (slot =
+ *             workgroup * waves per workgroup + wave), the turn waits that
+ *             found the turn not yet taken: [0] count, [1] polls, [2]
+ *             wall-clock ticks spent (dash_attn_bwd_wait_stats sums them)
  *   counters  B*Hq*N*W int32: the turn counter of every (batch, query head,
  *             dQ tile, slice) -- a slice is one 32-row x 32-feature block of
  *             the tile; after a deterministic backward each holds the number
@@ -173,6 +177,18 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v,
  * last backward that used this workspace fired, DASH_ERR_HIP on a runtime
  * error, else DASH_OK.  Reads 8 bytes of the workspace. */
 int dash_attn_bwd_check(const void* workspace, void* stream);
+
+/* Sums the turn-wait counters the last backward on this workspace left in it
+ * (after waiting for the stream): *waits = turn waits that found the turn not
+ * yet taken when first checked, *polls = re-polls of their counters, and
+ * *wait_seconds = wall-clock time those waits took, summed over the waves
+ * that made them.  These are the schedule's bubbles: time a wave could not
+ * proceed because an earlier contribution to a dQ tile was not yet added.
+ * The atomic reference makes no waits.  Any pointer may be NULL to skip that
+ * figure.  Returns DASH_ERR_NULL without a workspace, DASH_ERR_HIP on a
+ * runtime error. */
+int dash_attn_bwd_wait_stats(const void* workspace, void* stream, long long* waits,
+                             long long* polls, double* wait_seconds);
 
 /* Sets the device watchdog of the ordered reductions for the backward calls
  * planned after it, process-wide: a wave that has waited `seconds` of wall

@@ -32,7 +32,7 @@ SYMBOLS = (
     "dash_attn_bwd", "dash_attn_bwd_prepare", "dash_attn_bwd_run", "dash_attn_bwd_check", "dash_status_string",
     "dash_attn_bwd_grid_size", "dash_schedule_num_items",
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
-    "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog",
+    "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog", "dash_attn_bwd_wait_stats",
 )
 
 
@@ -81,6 +81,10 @@ def lib():
     L.dash_attn_bwd_check.restype = i
     L.dash_attn_set_watchdog.argtypes = [d]
     L.dash_attn_set_watchdog.restype = i
+    L.dash_attn_bwd_wait_stats.argtypes = [p, p, ctypes.POINTER(ctypes.c_longlong),
+                                           ctypes.POINTER(ctypes.c_longlong),
+                                           ctypes.POINTER(ctypes.c_double)]
+    L.dash_attn_bwd_wait_stats.restype = i
     L.dash_status_string.argtypes = [i]
     L.dash_status_string.restype = ctypes.c_char_p
     L.dash_attn_bwd_grid_size.argtypes = [i, i, i]
@@ -263,6 +267,18 @@ def dash_attn_bwd_check(workspace, stream=None):
     st = lib().dash_attn_bwd_check(_ptr(workspace), _stream(stream))
     if st != DASH_OK:
         raise DashError(st, "dash_attn_bwd_check")
+
+
+def dash_attn_bwd_wait_stats(workspace, stream=None):
+    """Turn waits of the last backward on this workspace: a dict with the
+    number of waits, their re-polls and the seconds they took (summed over
+    waves)."""
+    n, p, s = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_double()
+    st = lib().dash_attn_bwd_wait_stats(_ptr(workspace), _stream(stream), ctypes.byref(n),
+                                        ctypes.byref(p), ctypes.byref(s))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd_wait_stats")
+    return {"waits": n.value, "polls": p.value, "wait_seconds": s.value}
 
 
 def dash_attn_set_watchdog(seconds):

@@ -57,7 +57,7 @@ inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int T = 0, N = 0, NW = 0;
-  size_t ctrl = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, total = 0;
+  size_t ctrl = 0, waits = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, total = 0;
   long long n_counters = 0, n_rows = 0, n_dqacc = 0;
 };
 
@@ -89,6 +89,10 @@ int make_layout(int B, int Hq, int S, int D, Layout* L) {
   size_t off = 0;
   L->ctrl = off;
   off += round256(64 * sizeof(int));
+  // the kernel finds the wait counters right after the 64 control words
+  static_assert(64 * sizeof(int) % 256 == 0, "wait counters follow ctrl directly");
+  L->waits = off;
+  off += round256((size_t)dash::kWaitSlots * 4 * sizeof(unsigned long long));
   L->counters = off;
   off += round256((size_t)L->n_counters * sizeof(int));
   L->delta = off;
@@ -300,6 +304,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   pp.lse2 = (float*)(ws + L.lse2);
   pp.counters = (int*)(ws + L.counters);
   pp.ctrl = (int*)(ws + L.ctrl);
+  pp.waits = (unsigned long long*)(ws + L.waits);
   pp.dqacc = (float*)(ws + L.dqacc);
   pp.n_counters = L.n_counters;
   pp.n_dqacc = L.n_dqacc;
@@ -408,6 +413,30 @@ int dash_attn_bwd_check(const void* workspace, void* stream) {
       hipSuccess)
     return DASH_ERR_HIP;
   return flag[0] ? DASH_ERR_TIMEOUT : DASH_OK;
+}
+
+int dash_attn_bwd_wait_stats(const void* workspace, void* stream, long long* waits,
+                             long long* polls, double* wait_seconds) {
+  if (!workspace) return DASH_ERR_NULL;
+  DeviceInfo* dev = nullptr;
+  const int st = device_info(&dev);
+  if (st != DASH_OK) return st;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
+  std::vector<unsigned long long> v((size_t)dash::kWaitSlots * 4);
+  // the wait counters sit right after the 256 bytes of control words
+  if (hipMemcpy(v.data(), (const char*)workspace + 256, v.size() * sizeof(v[0]),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return DASH_ERR_HIP;
+  unsigned long long n = 0, p = 0, t = 0;
+  for (int s = 0; s < dash::kWaitSlots; ++s) {
+    n += v[4 * s];
+    p += v[4 * s + 1];
+    t += v[4 * s + 2];
+  }
+  if (waits) *waits = (long long)n;
+  if (polls) *polls = (long long)p;
+  if (wait_seconds) *wait_seconds = (double)t / (1000.0 * (double)dev->wall_khz);
+  return DASH_OK;
 }
 
 int dash_attn_set_watchdog(double seconds) {

@@ -3,7 +3,7 @@
 // Kernels:
 //   bwd_preprocess   per query row: -Dl = -rowsum(dO * O) and -lse/scale
 //                    (padded to whole tiles with 0 and -inf), zeroing of the
-//                    turn counters and dispatch state.
+//                    turn counters, the turn-wait counters and dispatch state.
 //   bwd_main         persistent backward: one workgroup per compute unit takes
 //                    items (a key/value chain, or a symmetric pair of chains)
 //                    from a device-wide counter and runs them tile by tile.
@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess(PreParams p) {
   const long long nthreads = (long long)gridDim.x * blockDim.x;
   for (long long x = tid; x < p.n_counters; x += nthreads) p.counters[x] = 0;
   if (tid < 64) p.ctrl[tid] = 0;
+  for (long long x = tid; x < 4LL * kWaitSlots; x += nthreads) p.waits[x] = 0;
   if (p.zero_dqacc) {
     f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     for (long long x = tid; x < p.n_dqacc / 4; x += nthreads)
@@ -206,7 +207,10 @@ __device__ __forceinline__ void wait_vm() {
 
 // Turn wait with a watchdog.  Executed by a whole wave; lane 0 polls.  Returns
 // false (and raises the workspace error flag) on timeout or if another wave
-// already raised it.
+// already raised it.  Only reached when the turn was not taken at the first
+// check; each such wait is counted in the wave's slot of the wait counters,
+// which follow the 64 control words in the workspace (one writer per slot, so
+// the additions never contend).
 __device__ __forceinline__ bool wait_turn(const int* cnt, int rank, int* ctrl,
                                           long long spin_ticks, int lane) {
   int ok = 1;
@@ -226,6 +230,14 @@ __device__ __forceinline__ bool wait_turn(const int* cnt, int rank, int* ctrl,
     if (!ok) {
       __hip_atomic_store(ctrl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(ctrl + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int slot = (int)blockIdx.x * ((int)blockDim.x >> 6) + ((int)threadIdx.x >> 6);
+    if (slot < kWaitSlots) {
+      unsigned long long* st = reinterpret_cast<unsigned long long*>(ctrl + 64) + 4 * slot;
+      const unsigned long long dt = (unsigned long long)(wall_clock64() - t0);
+      __hip_atomic_fetch_add(st, 1ULL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(st + 1, (unsigned long long)polls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(st + 2, dt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   ok = __shfl(ok, 0);

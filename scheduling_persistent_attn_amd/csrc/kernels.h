@@ -6,6 +6,10 @@
 
 namespace dash {
 
+// Wave slots of the turn-wait counters: the workspace region right after the
+// 64 control words, 4 uint64 per slot.
+constexpr int kWaitSlots = 4096;
+
 struct PreParams {
   const void* o;
   const void* dout;
@@ -14,6 +18,7 @@ struct PreParams {
   float* lse2;       // [B*Hq][NT]: -lse / scale, -inf past S
   int* counters;     // n_counters ints, zeroed
   int* ctrl;         // 64 ints, zeroed
+  unsigned long long* waits;  // kWaitSlots x 4, zeroed
   float* dqacc;      // zeroed when zero_dqacc (atomic schedule)
   long long n_counters;
   long long n_dqacc;

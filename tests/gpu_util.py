@@ -72,5 +72,7 @@ def read_counters(workspace, B, Hq, S, D):
     N = (S + T - 1) // T
     NW = T * D // 1024  # one counter per 32x32 slice of a dQ tile
     n = B * Hq * N * NW
+    # after the 64 control words and the 4096 x 4 uint64 wait counters
+    off = (256 + 4096 * 32) // 4
     ws = workspace.view(torch.int32)
-    return ws[64:64 + n].cpu().numpy().reshape(B, Hq, N, NW)
+    return ws[off:off + n].cpu().numpy().reshape(B, Hq, N, NW)

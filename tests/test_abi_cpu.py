@@ -48,6 +48,12 @@ def test_watchdog_setting_validation():
         dash.dash_attn_set_watchdog(ok)
 
 
+def test_wait_stats_needs_a_workspace():
+    n = ctypes.c_longlong()
+    assert dash.lib().dash_attn_bwd_wait_stats(None, None, ctypes.byref(n), None, None) \
+        == dash.DASH_ERR_NULL
+
+
 def test_status_strings():
     for s in range(8):
         assert dash.dash_status_string(s)
@@ -63,7 +69,9 @@ def test_tile_and_workspace_size():
     T, N = 128, 32
     n = dash.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, 1, 2)
     rows = B * Hq * N * T
-    want = 256 + B * Hq * N * (T * D // 1024) * 4 + 2 * rows * 4 + rows * D * 4
+    # control words, wait counters (4096 x 4 uint64), turn counters, the two
+    # per-row arrays and the fp32 dQ partial sums
+    want = 256 + 4096 * 32 + B * Hq * N * (T * D // 1024) * 4 + 2 * rows * 4 + rows * D * 4
     assert want <= n <= want + 5 * 256
     # ragged S rounds up to whole tiles
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 300, 64, 0, 0) > 0

@@ -54,3 +54,22 @@ def test_forced_timeout_is_reported_and_recovers():
         assert np.array_equal(a, b)
     cnt = gu.read_counters(ws, B, Hq, S, D)
     assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
+
+
+def test_turn_wait_counters():
+    # the rigid ascending order on a causal mask keeps chain i waiting for
+    # chains 0..i-1 at each of its dQ tiles, so waits are certain; the atomic
+    # reference makes none.  The counters are cleared by each call.
+    B, S, Hq, Hkv, D, causal = CASE
+    print("wait counters", CASE, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=2400)
+    o, lse = gu.run_forward(x, causal)
+    ws = dash.new_workspace(x["q"], x["k"], int(causal), dash.NAIVE)
+    gu.run_backward(x, o, lse, causal, dash.NAIVE, workspace=ws)
+    st = dash.dash_attn_bwd_wait_stats(ws)
+    print("naive", st, flush=True)
+    assert st["waits"] > 0 and st["wait_seconds"] > 0.0
+    assert st["polls"] >= 0
+    gu.run_backward(x, o, lse, causal, dash.ATOMIC, workspace=ws)
+    st = dash.dash_attn_bwd_wait_stats(ws)
+    assert st == {"waits": 0, "polls": 0, "wait_seconds": 0.0}
