@@ -341,8 +341,9 @@ __device__ __forceinline__ void stage_store(const PassStage<D, BQ, NW>& st, char
 // ordered reduction of a slice is pipelined over the three passes that follow
 // it: at the end of the first its turn (polled early in that pass) is checked
 // and its partial sum loaded; in the second its product is added and stored
-// (or, by the last contributor, written to dq in bf16); after the barrier of
-// the third its counter is published.  The round trips to the device-coherent
+// (or, by the last contributor, written to dq in bf16); in the third its
+// counter is published: after that pass's S/dP products when a task has four
+// or more passes, else right after its opening barrier.  The round trips to the device-coherent
 // level thus overlap with whole passes of computation.  The last pass of a KV
 // tile's run finishes the open slices before the tile changes.
 template <int D, int T, bool CAUSAL>
@@ -352,6 +353,12 @@ struct BwdCfg {
   static constexpr int QBP = NW / DB;    // 32-row blocks per pass
   static constexpr int BQ = 32 * QBP;    // query rows per pass
   static constexpr int NP = T / BQ;      // passes per task
+  // Where a stored slice is published.  After the next pass's S/dP products
+  // the stores have had the barrier and those products to be acknowledged,
+  // instead of stalling the top of the pass; the price is a third of a pass
+  // of hand-off delay, which tasks of four or more passes absorb (the next
+  // contributor of a slice is a task later) and tasks of two do not.
+  static constexpr bool PUBLISH_MID = NP >= 4;
   static constexpr int KBD = D / 16;     // k-blocks over the head dim
   static constexpr int KBT = T / 16;     // k-blocks over a tile of keys
   static constexpr int RBD = 2 * D;      // bytes per row of a Q/dO/K tile
@@ -560,10 +567,12 @@ __device__ __forceinline__ void acquire(const int* cnt, int expect, int polled, 
 //     (or, for the last contributor, written to dq) -- when ld_on;
 //   * slice `prev` (the previous pass): its turn, polled at the start of the
 //     pass, is checked at the end, then its partial sum is loaded into dq_ld
-//     for the next pass (zeros when there is nothing to add).
+//     for the next pass (zeros when there is nothing to add);
+//   * slice `rel` (stored at the end of the previous pass): with PUBLISH_MID
+//     its counter is bumped after the S/dP products -- when rel_on.
 // The partial-sum loads thus have most of a pass to arrive; the stores are
-// acknowledged at the wait at the top of the next pass, after which the
-// counter is bumped.  Everything from the first product to the dQ product has
+// acknowledged by the publish point (without PUBLISH_MID, the wait at the
+// top of the next pass).  Everything from the first product to the dQ product has
 // no branches, and scheduling barriers fix how far ahead of their products
 // the fragment reads are issued (without a slice two passes back the dQ
 // product is formed and dropped).  Writes dS of this pass into lS_cur.  When
@@ -574,6 +583,7 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
                                           float scale_log2e, bool masked, const unsigned* zb, const bf16x8* fk,
                                           const bf16x8* vB, const bf16x8* fkt, f32x16* dK, f32x16* dV,
                                           const Slice& ld, bool ld_on, f32x16& dq_ld, const Slice& prev,
+                                          const Slice& rel, bool rel_on,
                                           const int* poll_ptr, int poll_expect, int polled, int acc_bytes,
                                           const BwdParams& p, int rs, bf16* gdq,
                                           const PassStage<D, BwdCfg<D, T, CAUSAL>::BQ, BwdCfg<D, T, CAUSAL>::NW>* stage,
@@ -629,6 +639,19 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
       // without it the scheduler sinks each read next to its product and
       // every product waits for a full LDS round trip)
       __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- publish slice `rel`, whose partial-sum stores ended the previous
+  // pass: since then only its four partial-sum loads, this pass's staging
+  // loads and its turn poll were issued, so waiting until at most those are
+  // outstanding means the stores are acknowledged.
+  if constexpr (!ATOMIC && C::PUBLISH_MID) {
+    if (rel_on) {
+      order_point();
+      wait_vm<4 + 2 * PassStage<D, C::BQ, C::NW>::KQ + 2>();
+      order_point();
+      release(rel, lane);
     }
   }
 
@@ -835,11 +858,17 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         // issued last (when it ran a pass body), which the dQ product waits
         // for itself.  (The atomic reference publishes nothing, so its
         // fire-and-forget atomics are not waited for here.)
+        // this pass's inputs have arrived (the previous pass consumed them);
+        // unless they are published mid-pass, so have the partial-sum stores
+        // the previous pass ended with: wait for everything but its last
+        // four operations, the partial-sum loads the dQ product waits for
+        // itself.  (The atomic reference publishes nothing, so its
+        // fire-and-forget atomics are not waited for here.)
         if constexpr (!atomic_dq) {
-          if (acc_tail)
-            wait_vm<4>();
-          else
+          if (!acc_tail)
             __builtin_amdgcn_s_waitcnt(0);
+          else if constexpr (!C::PUBLISH_MID)
+            wait_vm<4>();
         }
         // the previous pass's LDS writes (dS, the staged inputs) are complete
         // once lgkmcnt drains; no global memory is shared between the waves
@@ -848,9 +877,11 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
         __builtin_amdgcn_s_barrier();
         order_point();
-        if (rel_pending) {
-          release(rel, lane);  // its stores completed at the wait above
-          rel_pending = false;
+        if constexpr (!C::PUBLISH_MID) {
+          if (rel_pending) {
+            release(rel, lane);  // its stores completed at the wait above
+            rel_pending = false;
+          }
         }
 
         // the previous slice's turn counter is polled right after the
@@ -896,12 +927,14 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
           zb[m] = z;
         }
         pass_body<D, T, CAUSAL, atomic_dq>(lQ, lO, lL, lS_cur, lS_ld, o, qg, hg, lane, p.scale_log2e, masked, zb,
-                                           fk, vB, fkt, dK, dV, ld, have_ld, dq_ld, prev, poll_ptr, poll_expect,
+                                           fk, vB, fkt, dK, dV, ld, have_ld, dq_ld, prev, rel, rel_pending,
+                                           poll_ptr, poll_expect,
                                            polled, acc_bytes, p, rsq, gdq, &stage, stage_next,
                                            smem + C::OFF_Q + (buf ^ 1) * C::Q_TILE,
                                            smem + C::OFF_DO + (buf ^ 1) * C::Q_TILE,
                                            smem + C::OFF_LD + (buf ^ 1) * 2 * 4 * BQ, w);
         acc_tail = true;
+        if constexpr (C::PUBLISH_MID) rel_pending = false;  // published inside the pass body
         if (have_ld && !atomic_dq) {
           rel = ld;
           rel_pending = true;
