@@ -41,10 +41,10 @@ Schedules (DASH technical summary, section 2.2):
 
 Grouped-query attention: Hq/Hkv = G query heads read one KV head.  One item
 serves one KV tile (or pair) for all G query heads so that dK/dV stay
-resident across the group; the task list of an item is the single-head list
-repeated per head, phase by phase for the symmetric shift (phase 1 for all
-heads, then the KV-p part of phase 2 for all heads, then the KV-(N-1-p) part
-for all heads).  Ranks are defined per (query head, dQ tile).
+resident across the group; the task list of an item takes every step of the
+single-head list for all G heads in turn (step outer, head inner), part by
+part for the symmetric shift (phase 1, the KV-p part of phase 2, the
+KV-(N-1-p) part).  Ranks are defined per (query head, dQ tile).
 
 Everything here is deliberately naive: task lists are materialised, and the
 arrival ranks are obtained by sorting the contributors of each dQ tile by the
@@ -121,13 +121,13 @@ def items(schedule, mask, N, G=1):
             ph1, ph2a, ph2b = symmetric_pair_parts(N, p)
             it = []
             for part in (ph1, ph2a, ph2b):
-                for g in range(G):
-                    it.extend((g, i, j) for (i, j) in part)
+                for (i, j) in part:
+                    it.extend((g, i, j) for g in range(G))
             out.append(it)
         return out
     for i in range(N):
         js = chain_q_order(schedule, mask, N, i)
-        out.append([(g, i, j) for g in range(G) for j in js])
+        out.append([(g, i, j) for j in js for g in range(G)])
     return out
 
 

@@ -23,10 +23,12 @@
 //                          triangles): j - i for Q < N/2, i for KV >= N/2
 //                          (section 2.2 B, symmetric shift; the fold geometry
 //                          is this library's reading of the two phases).
-// Item task lists for G > 1: the single-head list repeated per head (chains);
-// for the symmetric pair, phase 1 for every head, then the KV-p part of phase
-// 2 for every head, then the KV-(N-1-p) part for every head, which keeps the
-// lockstep free of conflicts with the same ranks as one head.
+// Item task lists for G > 1: every step of the single-head list is taken for
+// all G heads in turn (step outer, head inner) -- for the symmetric pair part
+// by part: phase 1, the KV-p part of phase 2, the KV-(N-1-p) part.  This keeps
+// each KV tile's run contiguous and the lockstep free of conflicts with the
+// same ranks as one head, and it spaces consecutive contributors to any dQ
+// tile a uniform G tasks apart, the most slack against drift between items.
 #pragma once
 
 #ifdef __HIPCC__
@@ -78,14 +80,14 @@ DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
       t.seg_begin = step == 0;
       t.seg_end = step == len_a - 1;
       if (step < G * h) {
-        t.g = step / h;
-        const int s = step - t.g * h;
+        const int s = step / G;
+        t.g = step - s * G;
         t.j = h + (p + s) % h;
         t.rank = s;
       } else {
-        const int k = step - G * h, l1 = h - p;
-        t.g = k / l1;
-        const int s = k - t.g * l1;
+        const int k = step - G * h;
+        const int s = k / G;
+        t.g = k - s * G;
         t.j = p + s;
         t.rank = s;
       }
@@ -94,8 +96,8 @@ DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
       t.i = N - 1 - p;
       t.seg_begin = k == 0;
       t.seg_end = k == G * l2 - 1;
-      t.g = k / l2;
-      const int s = k - t.g * l2;
+      const int s = k / G;
+      t.g = k - s * G;
       t.j = N - 1 - s;
       t.rank = t.i;
     }
@@ -106,8 +108,8 @@ DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
   const int i = item;
   const int L = chain_len(mask, N, i);
   t.i = i;
-  t.g = step / L;
-  const int s = step - t.g * L;
+  const int s = step / G;
+  t.g = step - s * G;
   t.seg_begin = step == 0;
   t.seg_end = step == G * L - 1;
   const int first = mask == MASK_CAUSAL ? i : 0;
