@@ -1,4 +1,5 @@
-"""The watchdog error path of the ordered reduction, forced from the host.
+"""The watchdog error path of the ordered reduction, forced from the host, and
+the turn-wait counters (the schedules' measured bubbles).
 
 With a zero wall-clock limit any turn wait longer than 64 polls gives up.  The
 naive (rigid ascending) order on a causal mask with 32 tiles makes chain i
@@ -73,3 +74,23 @@ def test_turn_wait_counters():
     gu.run_backward(x, o, lse, causal, dash.ATOMIC, workspace=ws)
     st = dash.dash_attn_bwd_wait_stats(ws)
     assert st == {"waits": 0, "polls": 0, "wait_seconds": 0.0}
+
+
+def test_shift_family_removes_the_rigid_orders_bubbles():
+    # the method's claim, measured: on a causal mask the rigid ascending order
+    # leaves waves waiting for earlier dQ contributions for a large share of
+    # the time, and the symmetric shift removes most of that waiting
+    B, S, Hq, Hkv, D, causal = CASE
+    print("bubbles", CASE, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=2500)
+    o, lse = gu.run_forward(x, causal)
+    waited = {}
+    for sched in (dash.NAIVE, dash.SYMMETRIC_SHIFT):
+        ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
+        gu.run_backward(x, o, lse, causal, sched, workspace=ws)  # warm-up
+        gu.run_backward(x, o, lse, causal, sched, workspace=ws)
+        waited[sched] = dash.dash_attn_bwd_wait_stats(ws)["wait_seconds"]
+    print("wave-seconds waiting: naive %.3g, symmetric shift %.3g"
+          % (waited[dash.NAIVE], waited[dash.SYMMETRIC_SHIFT]), flush=True)
+    assert waited[dash.NAIVE] > 0.0
+    assert waited[dash.SYMMETRIC_SHIFT] < 0.25 * waited[dash.NAIVE]
