@@ -70,3 +70,34 @@ def test_fullsize_sampled_parity(name):
             cnt = gu.read_counters(ws, B, Hq, S, D)
             assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
         del ws, dq, dk, dv
+
+
+def test_shift_at_the_residency_limit():
+    # a full mask with exactly as many tiles as the device runs workgroups:
+    # every shift item of the group is resident at once, the largest group the
+    # shift family accepts.  Checked through properties that hold at any size:
+    # two calls agree bit for bit, every turn counter ends at its contributor
+    # count, and the result agrees with the rigid order's (another reduction
+    # order of the same sums) within the oracle tolerance.
+    D = 128
+    T = dash.dash_attn_tile_size(4096, D)
+    grid = dash.dash_attn_bwd_grid_size(4096, D, 0)
+    B, S, Hq, Hkv = 1, grid * T, 2, 1
+    print("residency limit", grid, S, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=2600)
+    o, lse = gu.run_forward(x, False)
+    outs = {}
+    for sched in (dash.SHIFT, dash.SHIFT, dash.NAIVE):
+        ws = dash.new_workspace(x["q"], x["k"], 0, sched)
+        res = gu.run_backward(x, o, lse, False, sched, workspace=ws)
+        dash.dash_attn_bwd_check(ws)
+        cnt = gu.read_counters(ws, B, Hq, S, D)
+        assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, False))
+        outs.setdefault(sched, []).append([t.clone() for t in res])
+    a, b = outs[dash.SHIFT]
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+    for nm, u, v in zip(("dq", "dk", "dv"), a, outs[dash.NAIVE][0]):
+        e = gu.errors(gu.host64(u), gu.host64(v))
+        print("    shift vs naive %s rel-l2 %.3e max-abs(excess) %.3e" % ((nm,) + e[:2]))
+        assert gu.within(e), (nm, e)
