@@ -1,8 +1,11 @@
 """Run-to-run bit identity of every deterministic schedule on the GPU.
 
 20 runs per schedule rotate over three streams with a seeded, varying amount
-of unrelated GPU work queued before each call, so that workgroups reach the
-ordered reductions in different orders; dq/dk/dv must not change by a bit.
+of unrelated GPU work queued before each call, and every other run has a
+kernel on a fourth stream occupying compute units while the backward starts
+(it waits on nothing, so the backward's workgroups that cannot yet be resident
+only wait for it to drain), so that workgroups reach the ordered reductions in
+different orders and places; dq/dk/dv must not change by a bit.
 The atomic reference is run the same way and its spread is reported (it is
 the positive control that shows the harness can see non-determinism).
 """
@@ -45,16 +48,25 @@ def _runs(case, sched):
     o, lse = gu.run_forward(x, causal)
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream() for _ in range(3)]
+    busy = torch.cuda.Stream()
     rng = random.Random(1234 + sched)
     scratch = torch.ones(1 << 22, device="cuda")
+    big = torch.ones(1 << 27, device="cuda")  # 512 MiB: about a millisecond per pass over it
     outs = []
     for n in range(RUNS):
         s = streams[n % 3]
         _perturb(rng, s, scratch)
+        if n % 2:
+            # compute units occupied by unrelated work as the backward launches
+            busy.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(busy):
+                for _ in range(2):
+                    big.mul_(1.0001)
         ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
         with torch.cuda.stream(s):
             dq, dk, dv = gu.run_backward(x, o, lse, causal, sched, workspace=ws, stream=s)
         dash.dash_attn_bwd_check(ws, stream=s)
+        torch.cuda.current_stream().wait_stream(busy)
         outs.append(tuple(t.view(torch.int16).cpu().numpy().copy() for t in (dq, dk, dv)))
         if sched != dash.ATOMIC:
             cnt = gu.read_counters(ws, B, Hq, S, D)
