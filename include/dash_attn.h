@@ -184,11 +184,13 @@ int dash_attn_bwd_check(const void* workspace, void* stream);
  * *wait_seconds = wall-clock time those waits took, summed over the waves
  * that made them.  These are the schedule's bubbles: time a wave could not
  * proceed because an earlier contribution to a dQ tile was not yet added.
- * The atomic reference makes no waits.  Any pointer may be NULL to skip that
- * figure.  Returns DASH_ERR_NULL without a workspace, DASH_ERR_HIP on a
- * runtime error. */
-int dash_attn_bwd_wait_stats(const void* workspace, void* stream, long long* waits,
-                             long long* polls, double* wait_seconds);
+ * The atomic reference makes no waits.  Any output pointer may be NULL to
+ * skip that figure.  Returns DASH_ERR_NULL without a workspace,
+ * DASH_ERR_WORKSPACE if workspace_bytes does not cover the control words and
+ * the wait counters (256 + 4096 * 32 bytes), DASH_ERR_HIP on a runtime
+ * error. */
+int dash_attn_bwd_wait_stats(const void* workspace, size_t workspace_bytes, void* stream,
+                             long long* waits, long long* polls, double* wait_seconds);
 
 /* Sets the device watchdog of the ordered reductions for the backward calls
  * planned after it, process-wide: a wave that has waited `seconds` of wall

@@ -81,7 +81,7 @@ def lib():
     L.dash_attn_bwd_check.restype = i
     L.dash_attn_set_watchdog.argtypes = [d]
     L.dash_attn_set_watchdog.restype = i
-    L.dash_attn_bwd_wait_stats.argtypes = [p, p, ctypes.POINTER(ctypes.c_longlong),
+    L.dash_attn_bwd_wait_stats.argtypes = [p, sz, p, ctypes.POINTER(ctypes.c_longlong),
                                            ctypes.POINTER(ctypes.c_longlong),
                                            ctypes.POINTER(ctypes.c_double)]
     L.dash_attn_bwd_wait_stats.restype = i
@@ -274,8 +274,9 @@ def dash_attn_bwd_wait_stats(workspace, stream=None):
     number of waits, their re-polls and the seconds they took (summed over
     waves)."""
     n, p, s = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_double()
-    st = lib().dash_attn_bwd_wait_stats(_ptr(workspace), _stream(stream), ctypes.byref(n),
-                                        ctypes.byref(p), ctypes.byref(s))
+    st = lib().dash_attn_bwd_wait_stats(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(stream), ctypes.byref(n), ctypes.byref(p),
+                                        ctypes.byref(s))
     if st != DASH_OK:
         raise DashError(st, "dash_attn_bwd_wait_stats")
     return {"waits": n.value, "polls": p.value, "wait_seconds": s.value}

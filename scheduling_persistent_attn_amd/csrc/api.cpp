@@ -415,9 +415,11 @@ int dash_attn_bwd_check(const void* workspace, void* stream) {
   return flag[0] ? DASH_ERR_TIMEOUT : DASH_OK;
 }
 
-int dash_attn_bwd_wait_stats(const void* workspace, void* stream, long long* waits,
-                             long long* polls, double* wait_seconds) {
+int dash_attn_bwd_wait_stats(const void* workspace, size_t workspace_bytes, void* stream,
+                             long long* waits, long long* polls, double* wait_seconds) {
   if (!workspace) return DASH_ERR_NULL;
+  if (workspace_bytes < 256 + (size_t)dash::kWaitSlots * 4 * sizeof(unsigned long long))
+    return DASH_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   const int st = device_info(&dev);
   if (st != DASH_OK) return st;

@@ -49,9 +49,14 @@ def test_watchdog_setting_validation():
 
 
 def test_wait_stats_needs_a_workspace():
+    # both refusals happen before any device access
     n = ctypes.c_longlong()
-    assert dash.lib().dash_attn_bwd_wait_stats(None, None, ctypes.byref(n), None, None) \
+    L = dash.lib()
+    assert L.dash_attn_bwd_wait_stats(None, 1 << 20, None, ctypes.byref(n), None, None) \
         == dash.DASH_ERR_NULL
+    buf = ctypes.create_string_buffer(256)
+    assert L.dash_attn_bwd_wait_stats(ctypes.cast(buf, ctypes.c_void_p), 256, None,
+                                      ctypes.byref(n), None, None) == dash.DASH_ERR_WORKSPACE
 
 
 def test_status_strings():
