@@ -137,12 +137,19 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * Determinism contract (schedules 0-3): for fixed inputs, shape, mask,
  * schedule and library binary, dq/dk/dv are bitwise identical across calls,
  * streams and timing.  Different schedules may differ in the last bits.
- * dK/dV of a key/value head are summed over its query heads in ascending
- * order inside one unit.  The dQ tile j of query head h is reduced in the
- * order given by the schedule (see enum dash_schedule) using per-tile turn
- * counters in the workspace.
+ * dK/dV of a key/value tile are summed over its query heads inside one unit,
+ * in the unit's fixed task order (each query tile of the walk taken for all
+ * heads in turn).  The dQ tile j of query head h is reduced in the order given
+ * by the schedule (see enum dash_schedule) using per-tile turn counters in
+ * the workspace.
  *
- * The workspace must not be shared by concurrently running calls. */
+ * The workspace must not be shared by concurrently running calls.  Backward
+ * calls that overlap in time on one device (different streams with no
+ * ordering between them) share its compute units: the shift family needs a
+ * whole group of items resident at once, so two such calls near the residency
+ * limit can each hold units the other's items wait for.  Nothing hangs (every
+ * wait is bounded by the watchdog), but the calls then fail with
+ * DASH_ERR_TIMEOUT; order such calls with a stream or events. */
 int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk,
                   void* dv, int B, int Hq, int Hkv, int S, int D, int mask,
