@@ -120,6 +120,50 @@ def test_backward_parity_all_schedules(case):
             assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
 
 
+
+def _random_cases(n, seed=4242):
+    """Seeded shapes: batch, ragged sequence lengths across both tile sizes,
+    grouped-query ratios up to 7, both head dims and both masks."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        D = rng.choice([64, 128])
+        G = rng.choice([1, 1, 2, 3, 4, 7])
+        Hkv = rng.choice([1, 2])
+        S = rng.randint(1, 900)
+        out.append((rng.choice([1, 2]), S, G * Hkv, Hkv, D, rng.random() < 0.5))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(12), ids=lambda c: "B%dS%dH%d-%dD%d%s" % (
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "f"))
+def test_backward_parity_random_shapes(case):
+    # every applicable schedule against the oracle, element by element, and a
+    # second call of the best-balanced one bit for bit
+    B, S, Hq, Hkv, D, causal = case
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=3000 + S)
+    h = {k: gu.host64(v) for k, v in x.items()}
+    dq_ref, dk_ref, dv_ref = oa.attention_backward(h["q"], h["k"], h["v"], h["do"], causal)
+    o, lse = gu.run_forward(x, causal)
+    last = None
+    for sched in _schedules(causal, S, D):
+        print("random", case, "schedule", sched, flush=True)
+        ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
+        out = gu.run_backward(x, o, lse, causal, sched, workspace=ws)
+        dash.dash_attn_bwd_check(ws)
+        for name, got, ref in zip(("dq", "dk", "dv"), out, (dq_ref, dk_ref, dv_ref)):
+            e = gu.errors(gu.host64(got), ref)
+            assert gu.within(e), (name, sched, e)
+        if sched != dash.ATOMIC:
+            cnt = gu.read_counters(ws, B, Hq, S, D)
+            assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
+            last = (sched, ws, [t.clone() for t in out])
+    sched, ws, first = last
+    again = gu.run_backward(x, o, lse, causal, sched, workspace=ws)
+    for a, b in zip(first, again):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
 def test_backward_from_oracle_forward():
     # the backward alone, fed the oracle's O (rounded to bf16) and LSE
     case = (1, 512, 4, 1, 128, True)
