@@ -2,8 +2,10 @@
 
 The persistent kernel reduces the dQ slice of pass x in three stages: during
 pass x+1 it waits for the slice's turn and loads the partial sum; during pass
-x+2 it adds and stores; after the barrier that opens pass x+3 it publishes
-rank + 1 on the slice's counter.  The last pass of a key/value tile's run
+x+2 it adds and stores; during pass x+3 it publishes rank + 1 on the slice's
+counter (right after the pass's opening barrier, or after its S/dP products
+when a task has four or more passes) -- in both cases before that pass's own
+turn wait, which is the order the model below replays.  The last pass of a key/value tile's run
 stores the pending slices, publishes them, and only then waits for its own
 turn.  This test replays that order of operations for every item of every
 schedule (one worker per item, as the shift family requires) and checks that
