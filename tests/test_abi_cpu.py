@@ -319,3 +319,21 @@ def test_sim_report_closed_forms(capsys):
     assert sym["critical_path"] == 264.0 and sym["lemma1_violations"] == 0
     assert abs(sym["efficiency"] - 1.0) < 1e-12
     assert not any(r["deadlock"] for r in rows)
+
+
+def test_library_schedule_equals_hand_written_g2_table():
+    # the closed forms of the library against the hand-written G = 2, N = 4
+    # table (step outer, head inner), independently of the oracle
+    import json
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "schedules_n4_g2.json")))
+    N, G = gold["N"], gold["G"]
+    names = {"naive": 0, "descending": 1, "shift": 2, "symmetric": 3, "atomic": 4}
+    for key, rows in gold["items"].items():
+        name, mname = key.split("_")
+        s, m = names[name], {"full": 0, "causal": 1}[mname]
+        assert dash.dash_schedule_num_items(m, s, N) == len(rows), key
+        for n, row in enumerate(rows):
+            want = [tuple(int(v) for v in t.split(",")) for t in row.split()]
+            assert dash.dash_schedule_item_len(m, s, N, G, n) == len(want), (key, n)
+            got = [dash.dash_schedule_task(m, s, N, G, n, st) for st in range(len(want))]
+            assert got == want, (key, n)

@@ -238,3 +238,61 @@ def test_planted_wrong_mask_direction_is_caught(monkeypatch):
     bad = oa.attention_backward(q, k, v, do, True)
     # the closed form "dQ of causal row 0 is zero" no longer holds
     assert np.max(np.abs(bad[0][:, 0])) > 1e-6 or np.max(np.abs(bad[1] - good[1])) > 1e-6
+
+
+# --- the sampled form used by the full-size GPU tests ------------------------
+#
+# attention_backward_sampled(kv_heads=[kv]) must equal, element by element, the
+# slices of the whole-problem attention_backward that belong to key/value head
+# kv: dq of query heads kv*G .. kv*G+G-1, dk and dv of head kv, for every batch
+# entry.  attention_backward itself is pinned above (finite differences,
+# torch autograd), so this pins the sampled form to them.
+
+def _sampled_mismatch(sampled_fn, causal, rows=None):
+    rng = np.random.default_rng(11)
+    B, S, Hq, Hkv, D = 2, 9, 6, 2, 4
+    G = Hq // Hkv
+    q = _rand((B, S, Hq, D), rng)
+    k = _rand((B, S, Hkv, D), rng)
+    v = _rand((B, S, Hkv, D), rng)
+    do = _rand((B, S, Hq, D), rng)
+    dq, dk, dv = oa.attention_backward(q, k, v, do, causal)
+    got = sampled_fn(q, k, v, do, causal, list(range(Hkv)), q_rows=rows)
+    worst = 0.0
+    for kv in range(Hkv):
+        sdq, sdk, sdv = got[kv]
+        want_dq = dq[:, :, kv * G:(kv + 1) * G]
+        if rows is not None:
+            want_dq = want_dq[:, rows]
+        if sdq.shape != want_dq.shape or sdk.shape != dk[:, :, kv].shape:
+            return float("inf")
+        worst = max(worst, np.max(np.abs(sdq - want_dq)), np.max(np.abs(sdk - dk[:, :, kv])),
+                    np.max(np.abs(sdv - dv[:, :, kv])))
+    return worst
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_equals_whole_problem(causal):
+    assert _sampled_mismatch(oa.attention_backward_sampled, causal) < 1e-12
+    assert _sampled_mismatch(oa.attention_backward_sampled, causal, rows=[0, 4, 8]) < 1e-12
+
+
+def test_planted_sampled_head_mistakes_are_caught():
+    # every key/value head served by head 0's data
+    def kv0(q, k, v, do, causal, kv_heads, q_rows=None):
+        r = oa.attention_backward_sampled(q, k, v, do, causal, [0], q_rows=q_rows)
+        return {kv: r[0] for kv in kv_heads}
+
+    # the query heads of key/value head kv taken as kv .. kv+G-1
+    def shifted_heads(q, k, v, do, causal, kv_heads, q_rows=None):
+        G = q.shape[2] // k.shape[2]
+        out = {}
+        for kv in kv_heads:
+            hs = list(range(kv, kv + G))
+            r = oa.attention_backward_sampled(q[:, :, hs], k[:, :, kv:kv + 1], v[:, :, kv:kv + 1],
+                                              do[:, :, hs], causal, [0], q_rows=q_rows)
+            out[kv] = r[0]
+        return out
+
+    for fn in (kv0, shifted_heads):
+        assert _sampled_mismatch(fn, True) > 1e-6

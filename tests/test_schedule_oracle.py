@@ -242,3 +242,87 @@ def test_oracle_selection_closed_forms():
     # on one chain per worker takes N c
     s, res = dag.select(sch.FULL, N, P=N, c=c, r=0.0)
     assert s == sch.SHIFT and res["makespan"] == N * c
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query items: the hand-written G = 2, N = 4 table pins the task order
+# inside an item (step outer, head inner; part by part for the symmetric pair).
+
+GOLDEN_G2 = os.path.join(os.path.dirname(__file__), "golden", "schedules_n4_g2.json")
+G2_KEYS = {"naive": sch.NAIVE, "descending": sch.DESCENDING_Q, "shift": sch.SHIFT,
+           "symmetric": sch.SYMMETRIC_SHIFT, "atomic": sch.ATOMIC}
+
+
+def _parse_item(text):
+    return [tuple(int(v) for v in t.split(",")) for t in text.split()]
+
+
+def _g2_mismatches(items_fn, ranks_fn):
+    """Keys of the G = 2 table whose items or ranks differ from the given
+    item and rank functions (an empty list when all agree)."""
+    gold = json.load(open(GOLDEN_G2))
+    N, G = gold["N"], gold["G"]
+    bad = []
+    for key, rows in gold["items"].items():
+        name, mname = key.split("_")
+        s, m = G2_KEYS[name], MASKS[mname]
+        want = [_parse_item(r) for r in rows]
+        its = items_fn(s, m, N, G)
+        rk = ranks_fn(s, m, N, G)
+        got = [[(g, i, j, rk[(g, i, j)]) for (g, i, j) in it] for it in its]
+        if got != want:
+            bad.append(key)
+    return bad
+
+
+def test_golden_n4_g2():
+    assert _g2_mismatches(sch.items, sch.ranks) == []
+
+
+def test_planted_head_outer_order_is_caught():
+    # the earlier head-outer order (each walk for one head, then the next)
+    # covers the same tasks with the same ranks; only the table tells it apart
+    def head_outer(s, m, N, G):
+        return [sorted(it, key=lambda t: t[0]) for it in sch.items(s, m, N, G)]
+    bad = _g2_mismatches(head_outer, sch.ranks)
+    assert len(bad) == len(json.load(open(GOLDEN_G2))["items"])
+
+
+# ---------------------------------------------------------------------------
+# The causal diagonal weight.  With c_diag != c the closed forms of one group
+# with a worker per item (derived by hand from the event graph):
+#   causal SHIFT: chain i starts on its diagonal tile and never waits, so it
+#     ends at c_diag + (N-1-i) c + (N-i) r; the critical path is chain 0's,
+#     c_diag + (N-1) c + N r;
+#   SYMMETRIC_SHIFT: every pair meets its two diagonal tiles at the same two
+#     lockstep steps (the first of phase 2 and the last), so the lockstep
+#     holds and the critical path is 2 c_diag + (N-1) c + (N+1) r;
+#   total work: N diagonal tiles, N(N-1)/2 others, one reduction per task.
+
+DIAG_CASES = [(2, 5.0, 2.0, 1.0), (4, 5.0, 2.0, 1.0), (8, 3.0, 7.0, 0.5), (6, 4.0, 1.0, 0.0)]
+
+
+@pytest.mark.parametrize("N,c,cd,r", DIAG_CASES)
+def test_dag_causal_diagonal_weight(N, c, cd, r):
+    res = dag.simulate(sch.SHIFT, sch.CAUSAL, N, c=c, c_diag=cd, r=r)
+    assert not res["deadlock"]
+    assert res["makespan"] == cd + (N - 1) * c + N * r
+    assert res["total_work"] == N * cd + N * (N - 1) // 2 * c + N * (N + 1) // 2 * r
+    assert res["violations"] == 0
+    rep = dag.replay(sch.SHIFT, sch.CAUSAL, N, 1, 1, N, "static", c, cd, r)
+    for i in range(N):
+        assert rep["times"][(0, 0, i, N - 1)][3] == cd + (N - 1 - i) * c + (N - i) * r
+    res = dag.simulate(sch.SYMMETRIC_SHIFT, sch.CAUSAL, N, c=c, c_diag=cd, r=r)
+    assert not res["deadlock"]
+    assert res["makespan"] == 2 * cd + (N - 1) * c + (N + 1) * r
+    assert res["violations"] == 0
+
+
+def test_planted_diagonal_weight_off_by_one_is_caught(monkeypatch):
+    # the diagonal weight moved to the tile next to the diagonal
+    def shifted(mask, i, j, c, c_diag):
+        return c_diag if (mask == sch.CAUSAL and i == j + 1) else c
+    monkeypatch.setattr(dag, "task_cost", shifted)
+    N, c, cd, r = DIAG_CASES[1]
+    res = dag.simulate(sch.SHIFT, sch.CAUSAL, N, c=c, c_diag=cd, r=r)
+    assert res["makespan"] != cd + (N - 1) * c + N * r
