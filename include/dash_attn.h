@@ -91,7 +91,10 @@ enum dash_status {
                                  with a full mask or an odd tile count       */
   DASH_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required     */
   DASH_ERR_HIP = 6,           /* a HIP runtime call or launch failed         */
-  DASH_ERR_TIMEOUT = 7        /* the device watchdog fired during a backward */
+  DASH_ERR_TIMEOUT = 7,       /* the device watchdog fired during a backward */
+  DASH_ERR_NOT_PREPARED = 8   /* dash_attn_bwd_run found a workspace that
+                                 dash_attn_bwd_prepare had not reset since
+                                 the previous run; nothing was computed      */
 };
 
 /* Query-tile and key/value-tile edge T used for a problem (both sides use the
@@ -101,8 +104,10 @@ int dash_attn_tile_size(int S, int D);
 
 /* Bytes of workspace dash_attn_bwd needs for these arguments, or 0 if the
  * arguments are invalid.  Layout (offsets rounded up to 256 bytes):
- *   ctrl      64 x int32   [0] work-dispatch counter, [1] watchdog flag,
- *                          [2] number of waits that timed out
+ *   ctrl      64 x int32   [0] work-dispatch counter, [1] error flag
+ *                          (watchdog or not prepared), [2] number of waits
+ *                          that timed out, [3] always zero, [4] set when a
+ *                          run found the workspace not prepared
  *   waits     4096 x 4 uint64: per wave of the persistent grid (slot =
  *             workgroup * waves per workgroup + wave), the turn waits that
  *             found the turn not yet taken: [0] count, [1] polls, [2]
@@ -168,9 +173,12 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * dash_attn_bwd_run: the persistent backward over the schedule's items (and,
  * for ATOMIC, the pass that converts the fp32 accumulator to bf16 dq).  It
  * requires that dash_attn_bwd_prepare ran on this workspace, with the same
- * shape, mask and schedule, after the previous run: the turn counters must
- * start at zero, else the ordered reduction waits until the watchdog fires
- * (DASH_ERR_TIMEOUT from dash_attn_bwd_check). */
+ * shape, mask and schedule, after the previous run.  A run on a workspace
+ * that was not prepared again after an earlier run finds the dispatch
+ * counter already used: it computes nothing, leaves dq/dk/dv untouched, and
+ * dash_attn_bwd_check then returns DASH_ERR_NOT_PREPARED.  (A prepare with a
+ * different shape, mask or schedule is not detected; the results are then
+ * undefined.) */
 int dash_attn_bwd_prepare(const void* o, const void* dout, const float* lse, int B,
                           int Hq, int Hkv, int S, int D, int mask, int schedule,
                           void* workspace, size_t workspace_bytes, void* stream);
@@ -180,9 +188,10 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v,
                       int Hq, int Hkv, int S, int D, int mask, int schedule,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Waits for the stream, then reports DASH_ERR_TIMEOUT if the watchdog of the
- * last backward that used this workspace fired, DASH_ERR_HIP on a runtime
- * error, else DASH_OK.  Reads 8 bytes of the workspace. */
+/* Waits for the stream, then reports DASH_ERR_NOT_PREPARED if the last
+ * backward run on this workspace found it not prepared, DASH_ERR_TIMEOUT if
+ * its watchdog fired, DASH_ERR_HIP on a runtime error, else DASH_OK.  Reads
+ * 16 bytes of the workspace. */
 int dash_attn_bwd_check(const void* workspace, void* stream);
 
 /* Sums the turn-wait counters the last backward on this workspace left in it

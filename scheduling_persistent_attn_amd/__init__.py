@@ -26,6 +26,7 @@ DASH_ERR_SCHEDULE_MASK = 4
 DASH_ERR_WORKSPACE = 5
 DASH_ERR_HIP = 6
 DASH_ERR_TIMEOUT = 7
+DASH_ERR_NOT_PREPARED = 8
 
 SYMBOLS = (
     "dash_attn_tile_size", "dash_attn_bwd_workspace_size", "dash_attn_fwd",
@@ -188,6 +189,8 @@ def _ptr(t):
 
 
 def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-d [B, S, H, D] tensors")
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     return B, S, Hq, Hkv, D
@@ -203,12 +206,50 @@ def _check_tensors(named, dtype):
             raise ValueError("%s must be contiguous" % name)
 
 
+def _check_layout(dims, q_like=(), kv_like=(), row_like=()):
+    """Shapes and device of every tensor the C ABI will read or write through
+    a raw pointer: q_like are [B, S, Hq, D], kv_like [B, S, Hkv, D] and
+    row_like [B, Hq, S]; all on one GPU.  A mismatch would make a kernel read
+    or write past an allocation, so it raises ValueError before any call."""
+    B, S, Hq, Hkv, D = dims
+    want = {"q": (B, S, Hq, D), "kv": (B, S, Hkv, D), "row": (B, Hq, S)}
+    named = ([(n, t, "q") for n, t in q_like] + [(n, t, "kv") for n, t in kv_like]
+             + [(n, t, "row") for n, t in row_like])
+    device = None
+    for name, t, kind in named:
+        if t is None:
+            continue
+        if tuple(t.shape) != want[kind]:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), want[kind]))
+    for name, t, _ in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s must be a GPU tensor (is on %s)" % (name, t.device))
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError("%s is on %s, the other tensors on %s" % (name, t.device, device))
+    return device
+
+
+def _check_workspace(workspace, device):
+    if workspace is None:
+        return
+    if workspace.dtype.itemsize != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous byte tensor")
+    if device is not None and workspace.device != device:
+        raise ValueError("workspace is on %s, the tensors on %s" % (workspace.device, device))
+
+
 def dash_attn_fwd(q, k, v, o, lse, mask, stream=None):
     """Forward into preallocated o [B,S,Hq,D] bf16 and lse [B,Hq,S] fp32."""
     import torch
     _check_tensors([("q", q), ("k", k), ("v", v), ("o", o)], torch.bfloat16)
     _check_tensors([("lse", lse)], torch.float32)
-    B, S, Hq, Hkv, D = _dims(q, k)
+    dims = _dims(q, k)
+    _check_layout(dims, [("q", q), ("o", o)], [("k", k), ("v", v)], [("lse", lse)])
+    B, S, Hq, Hkv, D = dims
     st = lib().dash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                              B, Hq, Hkv, S, D, int(mask), _stream(stream))
     if st != DASH_OK:
@@ -222,7 +263,11 @@ def dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, workspace,
     _check_tensors([("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout),
                     ("dq", dq), ("dk", dk), ("dv", dv)], torch.bfloat16)
     _check_tensors([("lse", lse)], torch.float32)
-    B, S, Hq, Hkv, D = _dims(q, k)
+    dims = _dims(q, k)
+    dev = _check_layout(dims, [("q", q), ("o", o), ("dout", dout), ("dq", dq)],
+                        [("k", k), ("v", v), ("dk", dk), ("dv", dv)], [("lse", lse)])
+    _check_workspace(workspace, dev)
+    B, S, Hq, Hkv, D = dims
     st = lib().dash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                              _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(mask),
                              int(schedule), _ptr(workspace),
@@ -234,13 +279,16 @@ def dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, workspace,
 
 def dash_attn_bwd_prepare(o, dout, lse, q_shape, kv_heads, mask, schedule, workspace,
                           stream=None):
-    """First phase of dash_attn_bwd (delta, lse*log2e, counter reset).
+    """First phase of dash_attn_bwd (the per-row values, counter reset).
     q_shape is (B, S, Hq, D); kv_heads is Hkv."""
     import torch
     _check_tensors([("o", o), ("dout", dout)], torch.bfloat16)
     _check_tensors([("lse", lse)], torch.float32)
     B, S, Hq, D = q_shape
-    st = lib().dash_attn_bwd_prepare(_ptr(o), _ptr(dout), _ptr(lse), B, Hq, int(kv_heads), S,
+    Hkv = int(kv_heads)
+    dev = _check_layout((B, S, Hq, Hkv, D), [("o", o), ("dout", dout)], [], [("lse", lse)])
+    _check_workspace(workspace, dev)
+    st = lib().dash_attn_bwd_prepare(_ptr(o), _ptr(dout), _ptr(lse), B, Hq, Hkv, S,
                                      D, int(mask), int(schedule), _ptr(workspace),
                                      workspace.numel() if workspace is not None else 0,
                                      _stream(stream))
@@ -253,7 +301,11 @@ def dash_attn_bwd_run(q, k, v, dout, dq, dk, dv, mask, schedule, workspace, stre
     import torch
     _check_tensors([("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk),
                     ("dv", dv)], torch.bfloat16)
-    B, S, Hq, Hkv, D = _dims(q, k)
+    dims = _dims(q, k)
+    dev = _check_layout(dims, [("q", q), ("dout", dout), ("dq", dq)],
+                        [("k", k), ("v", v), ("dk", dk), ("dv", dv)])
+    _check_workspace(workspace, dev)
+    B, S, Hq, Hkv, D = dims
     st = lib().dash_attn_bwd_run(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
                                  _ptr(dv), B, Hq, Hkv, S, D, int(mask), int(schedule),
                                  _ptr(workspace),
@@ -309,7 +361,13 @@ def forward(q, k, v, causal):
     return o, lse
 
 
-def backward(q, k, v, o, dout, lse, causal, schedule=SHIFT, workspace=None, stream=None):
+def backward(q, k, v, o, dout, lse, causal, schedule=SHIFT, workspace=None, stream=None,
+             check=True):
+    """Allocates dq, dk, dv and runs dash_attn_bwd.  With check (the default)
+    it then waits for the stream and raises DashError if the device watchdog
+    fired, in which case the outputs would be undefined; with check=False the
+    call stays asynchronous and the caller must call dash_attn_bwd_check on
+    the workspace before trusting the result."""
     import torch
     mask = MASK_CAUSAL if causal else MASK_FULL
     if workspace is None:
@@ -318,4 +376,6 @@ def backward(q, k, v, o, dout, lse, causal, schedule=SHIFT, workspace=None, stre
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, workspace, stream)
+    if check:
+        dash_attn_bwd_check(workspace, stream)
     return dq, dk, dv

@@ -196,6 +196,7 @@ const char* dash_status_string(int status) {
     case DASH_ERR_WORKSPACE: return "workspace missing or too small";
     case DASH_ERR_HIP: return "HIP runtime error";
     case DASH_ERR_TIMEOUT: return "device watchdog fired in an ordered reduction";
+    case DASH_ERR_NOT_PREPARED: return "backward run on a workspace not prepared since the last run";
     default: return "unknown status";
   }
 }
@@ -408,10 +409,12 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v, const void* d
 int dash_attn_bwd_check(const void* workspace, void* stream) {
   if (!workspace) return DASH_ERR_NULL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
-  int flag[2] = {0, 0};
+  // ctrl[1] error flag, [2] timed-out waits, [3] always zero, [4] not-prepared mark
+  int flag[4] = {0, 0, 0, 0};
   if (hipMemcpy(flag, (const int*)workspace + 1, sizeof(flag), hipMemcpyDeviceToHost) !=
       hipSuccess)
     return DASH_ERR_HIP;
+  if (flag[3]) return DASH_ERR_NOT_PREPARED;
   return flag[0] ? DASH_ERR_TIMEOUT : DASH_OK;
 }
 

@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "lds_layout.h"
 #include "schedule.h"
 
 namespace dash {
@@ -63,52 +64,9 @@ __device__ __forceinline__ bf16x8 zero8() {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout.
-//
-// A tile is stored row-major in 256-byte "super-rows": a row of 256 bytes is
-// one super-row; rows of 128 bytes are paired (row r is the half r & 1 of
-// super-row r >> 1).  Each super-row holds 16 slots of 16 bytes and logical
-// slot U of super-row R sits at slot U ^ sw(R).  The LDS of gfx950 serves
-// 256 bytes per cycle from 64 four-byte banks; with
-//   sw(R) = ((a << 1) ^ (a << 2)) ^ b,  a = R & 3,
-//   b = (R >> 2) & 3 for 256-byte rows, (R >> 2) & 1 for 128-byte rows,
-// both access shapes of the kernel are free of bank conflicts: 16-byte reads
-// of one column in 16 consecutive rows, and the transposing 8-byte reads
-// (ds_read_b64_tr_b16) of 4 consecutive rows x 64 bytes.  sw depends only on
-// the low bits of the row, so moving by 16 rows is a constant offset.
-__device__ __forceinline__ int sw16(int R, int row_bytes) {
-  const int a = R & 3;
-  const int b = row_bytes == 256 ? ((R >> 2) & 3) : ((R >> 2) & 1);
-  return ((a << 1) ^ (a << 2)) ^ b;
-}
-
-// Byte offset of 16-byte chunk `chunk` of row `row` in a tile whose rows are
-// row_bytes (128 or 256) long.
-template <int RB>
-__device__ __forceinline__ int phys(int row, int chunk) {
-  static_assert(RB == 128 || RB == 256, "row length");
-  if constexpr (RB == 256) {
-    return row * 256 + ((chunk ^ sw16(row, 256)) << 4);
-  } else {
-    const int R = row >> 1;
-    const int U = ((row & 1) << 3) | chunk;
-    return R * 256 + ((U ^ sw16(R, 128)) << 4);
-  }
-}
-
-// Inverse for the loader: physical slot `slot` of super-row R holds
-// (row, chunk).
-template <int RB>
-__device__ __forceinline__ void slot_source(int R, int slot, int* row, int* chunk) {
-  if constexpr (RB == 256) {
-    *row = R;
-    *chunk = slot ^ sw16(R, 256);
-  } else {
-    const int U = slot ^ sw16(R, 128);
-    *row = 2 * R + (U >> 3);
-    *chunk = U & 7;
-  }
-}
+// LDS tiles use the swizzled layout of lds_layout.h: 16-byte row reads of one
+// column in 16 consecutive rows and the transposing 8-byte reads of 4 rows x
+// 64 bytes are both free of bank conflicts.
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -243,6 +201,24 @@ __device__ __forceinline__ bool wait_turn(const int* cnt, int rank, int* ctrl,
   ok = __shfl(ok, 0);
   order_point();
   return ok != 0;
+}
+
+// The next item index from the work-dispatch counter ctrl[0] (called by one
+// thread per workgroup).  Each launch on a prepared workspace ends with one
+// draw past the end per workgroup, so its draws are all below total + grid.  A
+// launch that finds the counter at or past that on its first draw runs on a
+// workspace the preprocess did not reset since the last launch (a run without
+// its prepare): it raises the error flag ctrl[1] and the not-prepared mark
+// ctrl[4], and every workgroup drains at once without touching the outputs.
+// Once ctrl[1] is up (also by the watchdog) no further item is handed out.
+__device__ __forceinline__ int next_item(int* ctrl, int total, bool first) {
+  int it = atomicAdd(ctrl, 1);
+  if (first && it >= total + (int)gridDim.x) {
+    __hip_atomic_store(ctrl + 4, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ctrl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (__hip_atomic_load(ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) it = total;
+  return it;
 }
 
 // Asynchronous copy of ROWS rows of a bf16 tensor with row stride rs
@@ -646,6 +622,15 @@ __device__ __forceinline__ void pass_body(const char* lQ, const char* lO, const 
   // pass: since then only its four partial-sum loads, this pass's staging
   // loads and its turn poll were issued, so waiting until at most those are
   // outstanding means the stores are acknowledged.
+  //   The count relies on this invariant: between the last store of `rel`
+  // and this point each wave issues exactly 4 accumulator loads (acc_load,
+  // always four b128 loads, out of range when nothing is added), 2 * KQ
+  // staging loads plus one per-row value load (stage_load issues them
+  // unconditionally, out of range when there is no next pass), and one turn
+  // poll: 4 + 2 * KQ + 2 vector-memory operations, none of them conditional.
+  // Vector-memory operations retire in issue order, so vmcnt <= that count
+  // means every older operation, the stores included, has completed.  The
+  // bit-identity tests at every workload size guard the count.
   if constexpr (!ATOMIC && C::PUBLISH_MID) {
     if (rel_on) {
       order_point();
@@ -713,24 +698,24 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
 
   // ---- per-lane LDS offsets ------------------------------------------------
   LaneOffs<D, T> o;
-  o.a = phys<C::RBD>(c, hg);
-  o.s = phys<C::RBS>(c, hg);
+  o.a = lds_phys<C::RBD>(c, hg);
+  o.s = lds_phys<C::RBS>(c, hg);
   // transposing reads of Q / dO: source lane s16 reads row 4hg + (s16 >> 2)
   // (+8 for the upper half), features 16(g16 & 1) + 4(s16 & 3) .. +3 of block 0
 #pragma unroll
   for (int h8 = 0; h8 < 2; ++h8) {
     const int col = 16 * (g16 & 1) + 4 * (s16 & 3);
-    o.tq[h8] = phys<C::RBD>(8 * h8 + 4 * hg + (s16 >> 2), col >> 3) + 2 * (col & 7);
+    o.tq[h8] = lds_phys<C::RBD>(8 * h8 + 4 * hg + (s16 >> 2), col >> 3) + 2 * (col & 7);
   }
   // transposing reads of K for dQ = dS K: keys 8hg + 4h4 + (s16 >> 2) of each
   // 16-key block, features of block db
 #pragma unroll
   for (int h4 = 0; h4 < 2; ++h4) {
     const int col = 32 * db + 16 * (g16 & 1) + 4 * (s16 & 3);
-    o.kt[h4] = phys<C::RBD>(8 * hg + 4 * h4 + (s16 >> 2), col >> 3) + 2 * (col & 7);
+    o.kt[h4] = lds_phys<C::RBD>(8 * hg + 4 * h4 + (s16 >> 2), col >> 3) + 2 * (col & 7);
   }
   // dS element writes: key 32w + c, row 4hg (+ the per-element constants)
-  o.wr = phys<C::RBS>(4 * hg, (32 * w + c) >> 3) + 2 * ((32 * w + c) & 7);
+  o.wr = lds_phys<C::RBS>(4 * hg, (32 * w + c) >> 3) + 2 * ((32 * w + c) & 7);
   // causal diagonal block: bit r set where key c comes after query row
   // 8(r >> 2) + 4hg + (r & 3) of the accumulator layout
   unsigned diag_bits = 0;
@@ -738,7 +723,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   for (int r = 0; r < 16; ++r) diag_bits |= (c > 8 * (r >> 2) + 4 * hg + (r & 3) ? 1u : 0u) << r;
   // loader: source (row, chunk) of the slot this lane fills in its first block
   int ldRow0, ldChunk0;
-  slot_source<C::RBD>(4 * w + (lane >> 4), lane & 15, &ldRow0, &ldChunk0);
+  lds_slot_source<C::RBD>(4 * w + (lane >> 4), lane & 15, &ldRow0, &ldChunk0);
 
   f32x16 dK[C::DB], dV[C::DB];
   // operands from the current KV tile, held for its whole run:
@@ -759,15 +744,12 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   f32x16 dq_ld = {};
   int sb = 0;  // dS buffer of the current pass (of three)
   bool acc_tail = false;  // the last four vector memory operations are partial-sum loads
+  bool first_item = true;
   for (;;) {
     __syncthreads();  // previous item's LDS use complete
     int* const misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
-    if (tid == 0) {
-      int it = atomicAdd(p.ctrl, 1);
-      if (__hip_atomic_load(p.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-        it = p.total_items;
-      misc[0] = it;
-    }
+    if (tid == 0) misc[0] = next_item(p.ctrl, p.total_items, first_item);
+    first_item = false;
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(misc[0]);
     if (item >= p.total_items) break;
@@ -853,11 +835,6 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         for (int kb = 0; kb < C::KBD; ++kb) asm volatile("" : "+a"(fk[kb]), "+a"(vB[kb]));
 #pragma unroll
         for (int kb = 0; kb < C::KBT; ++kb) asm volatile("" : "+a"(fkt[kb]));
-        // this pass's inputs and the previous pass's accumulator stores have
-        // completed: everything but the partial-sum loads the previous pass
-        // issued last (when it ran a pass body), which the dQ product waits
-        // for itself.  (The atomic reference publishes nothing, so its
-        // fire-and-forget atomics are not waited for here.)
         // this pass's inputs have arrived (the previous pass consumed them);
         // unless they are published mid-pass, so have the partial-sum stores
         // the previous pass ended with: wait for everything but its last

@@ -49,19 +49,6 @@ __device__ __forceinline__ f32x16 mfma_f(bf16x8 a, bf16x8 b, f32x16 c) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Physical slot `slot` of super-row R holds (row, chunk) of the tile.
-template <int RB>
-__device__ __forceinline__ void slot_src(int R, int slot, int* row, int* chunk) {
-  if constexpr (RB == 256) {
-    *row = R;
-    *chunk = slot ^ lds_sw16(R, 256);
-  } else {
-    const int U = slot ^ lds_sw16(R, 128);
-    *row = 2 * R + (U >> 3);
-    *chunk = U & 7;
-  }
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(FwdParams p) {
   constexpr int BQ = 256, NT = 512, BK = 128, RB = 2 * D;
@@ -109,7 +96,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // slot in its first block holds source (row0, chunk0), and the slot pattern
   // repeats every 4 NW super-rows
   int row0, chunk0;
-  slot_src<RB>(4 * w + (lane >> 4), lane & 15, &row0, &chunk0);
+  lds_slot_source<RB>(4 * w + (lane >> 4), lane & 15, &row0, &chunk0);
   const int krs = p.Hkv * D;
   const int voff = (row0 * krs + chunk0 * 8) * 2;
   const size_t head0 = ((size_t)b * S * p.Hkv + hk) * D;

@@ -35,4 +35,19 @@ __device__ __forceinline__ int lds_phys(int row, int chunk) {
   }
 }
 
+// Inverse, for the loaders: physical slot `slot` of super-row R holds 16-byte
+// chunk *chunk of row *row.
+template <int RB>
+__device__ __forceinline__ void lds_slot_source(int R, int slot, int* row, int* chunk) {
+  static_assert(RB == 128 || RB == 256, "row length");
+  if constexpr (RB == 256) {
+    *row = R;
+    *chunk = slot ^ lds_sw16(R, 256);
+  } else {
+    const int U = slot ^ lds_sw16(R, 128);
+    *row = 2 * R + (U >> 3);
+    *chunk = U & 7;
+  }
+}
+
 }  // namespace dash

@@ -40,8 +40,8 @@ def run_forward(x, causal):
     return o, lse
 
 
-def run_backward(x, o, lse, causal, schedule, workspace=None, stream=None):
-    return dash.backward(x["q"], x["k"], x["v"], o, x["do"], lse, causal, schedule,
+def run_backward(x, o, lse, causal, schedule, workspace=None, stream=None, check=True):
+    return dash.backward(x["q"], x["k"], x["v"], o, x["do"], lse, causal, schedule, check=check,
                          workspace=workspace, stream=stream)
 
 

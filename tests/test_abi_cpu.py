@@ -337,3 +337,47 @@ def test_library_schedule_equals_hand_written_g2_table():
             assert dash.dash_schedule_item_len(m, s, N, G, n) == len(want), (key, n)
             got = [dash.dash_schedule_task(m, s, N, G, n, st) for st in range(len(want))]
             assert got == want, (key, n)
+
+
+def test_binding_rejects_mismatched_tensors():
+    # every tensor's shape is checked against (B, S, Hq, D), (B, S, Hkv, D)
+    # and (B, Hq, S) before the C ABI gets raw pointers; CPU tensors with the
+    # right shapes are refused as not on a GPU
+    import torch
+    B, S, Hq, Hkv, D = 1, 8, 4, 2, 64
+    bf = torch.bfloat16
+
+    def mk(*shape, dtype=bf):
+        return torch.zeros(shape, dtype=dtype)
+
+    q, o, do, dq = (mk(B, S, Hq, D) for _ in range(4))
+    k, v, dk, dv = (mk(B, S, Hkv, D) for _ in range(4))
+    lse = mk(B, Hq, S, dtype=torch.float32)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    bad = {"v": mk(B, S - 1, Hkv, D), "o": mk(B, S, Hq, D // 2), "dout": mk(B, S, Hkv, D),
+           "dq": mk(B, S, Hq + 1, D), "dk": mk(B, S, Hq, D), "dv": mk(B, 2 * S, Hkv, D),
+           "lse": mk(B, S, Hq, dtype=torch.float32)}
+    args = dict(q=q, k=k, v=v, o=o, dout=do, lse=lse, dq=dq, dk=dk, dv=dv)
+    for name, t in bad.items():
+        a = dict(args)
+        a[name] = t
+        with pytest.raises(ValueError, match="shape"):
+            dash.dash_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"],
+                               a["dk"], a["dv"], 0, dash.SHIFT, ws)
+    with pytest.raises(ValueError, match="shape"):
+        dash.dash_attn_fwd(q, k, bad["v"], o, lse, 0)
+    with pytest.raises(ValueError, match="shape"):
+        dash.dash_attn_fwd(q, k, v, o, bad["lse"], 0)
+    with pytest.raises(ValueError, match="shape"):
+        dash.dash_attn_bwd_run(q, k, v, do, dq, bad["dk"], dv, 0, dash.SHIFT, ws)
+    with pytest.raises(ValueError, match="shape"):
+        dash.dash_attn_bwd_prepare(o, bad["dout"], lse, (B, S, Hq, D), Hkv, 0, dash.SHIFT, ws)
+    with pytest.raises(ValueError, match="GPU"):
+        dash.dash_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, 0, dash.SHIFT, ws)
+    with pytest.raises(ValueError, match="GPU"):
+        dash.dash_attn_fwd(q, k, v, o, lse, 0)
+
+
+def test_not_prepared_status():
+    assert dash.DASH_ERR_NOT_PREPARED == 8
+    assert "not prepared" in dash.dash_status_string(8)

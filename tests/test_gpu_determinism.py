@@ -6,8 +6,12 @@ kernel on a fourth stream occupying compute units while the backward starts
 (it waits on nothing, so the backward's workgroups that cannot yet be resident
 only wait for it to drain), so that workgroups reach the ordered reductions in
 different orders and places; dq/dk/dv must not change by a bit.
-The atomic reference is run the same way and its spread is reported (it is
-the positive control that shows the harness can see non-determinism).
+The atomic reference is run the same way at a full workload size, and at
+least one of its runs must differ (the positive control that shows the harness
+can see non-determinism).  One case has more items than the persistent grid
+has workgroups, so workgroups take further items as they finish, in an order
+that varies from run to run; the full-size cases are in
+test_gpu_determinism_fullsize.py.
 """
 
 import random
@@ -32,6 +36,7 @@ CASES = [
     (2, 1024, 4, 4, 64, False),
     (1, 2048, 8, 8, 128, False),
     (2, 1024, 16, 4, 128, True),  # 8 groups: one item queue per XCD
+    (2, 4096, 8, 8, 128, False),  # 512 chains on 256 workgroups: dynamic re-dispatch
 ]
 
 
@@ -95,11 +100,16 @@ def test_bit_identical_over_runs(case):
 
 
 def test_atomic_reference_spread():
-    case = CASES[2]
+    # the causal 8B-Llama-shaped layer (B=4 S=4096 Hq=32 Hkv=8 D=128): with
+    # 32768 dQ slices each summed from up to 32 unordered atomic contributions,
+    # the harness must see the order change
+    case = (4, 4096, 32, 8, 128, True)
+    print("atomic reference", case, flush=True)
     outs = _runs(case, dash.ATOMIC)
     differing = sum(1 for n in range(1, RUNS)
                     if not np.array_equal(outs[0][0], outs[n][0]))
     print("atomic reference: %d of %d runs differ from the first in dq" % (differing, RUNS - 1))
+    assert differing >= 1
 
 
 @pytest.mark.parametrize("sched", [dash.SHIFT, dash.SYMMETRIC_SHIFT])

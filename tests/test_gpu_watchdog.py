@@ -40,7 +40,7 @@ def test_forced_timeout_is_reported_and_recovers():
     dash.dash_attn_bwd_check(ws)
     try:
         dash.dash_attn_set_watchdog(0.0)
-        gu.run_backward(x, o, lse, causal, dash.NAIVE, workspace=ws)
+        gu.run_backward(x, o, lse, causal, dash.NAIVE, workspace=ws, check=False)
         with pytest.raises(dash.DashError) as e:
             dash.dash_attn_bwd_check(ws)
         assert e.value.status == dash.DASH_ERR_TIMEOUT
@@ -94,3 +94,29 @@ def test_shift_family_removes_the_rigid_orders_bubbles():
           % (waited[dash.NAIVE], waited[dash.SYMMETRIC_SHIFT]), flush=True)
     assert waited[dash.NAIVE] > 0.0
     assert waited[dash.SYMMETRIC_SHIFT] < 0.25 * waited[dash.NAIVE]
+
+
+def test_run_without_prepare_is_reported():
+    # a second dash_attn_bwd_run on a workspace that dash_attn_bwd_prepare has
+    # not reset computes nothing, leaves the outputs untouched and is reported
+    # as DASH_ERR_NOT_PREPARED; a prepared run afterwards is bit-identical
+    B, S, Hq, Hkv, D, causal = CASE
+    print("run without prepare", CASE, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=2700)
+    o, lse = gu.run_forward(x, causal)
+    for sched in (dash.SHIFT, dash.ATOMIC):
+        ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
+        good = [t.clone() for t in gu.run_backward(x, o, lse, causal, sched, workspace=ws)]
+        dq, dk, dv = (torch.full_like(t, 7.0) for t in good)
+        dash.dash_attn_bwd_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, int(causal), sched, ws)
+        with pytest.raises(dash.DashError) as e:
+            dash.dash_attn_bwd_check(ws)
+        assert e.value.status == dash.DASH_ERR_NOT_PREPARED
+        for t in (dq, dk, dv):
+            assert bool((t == 7.0).all())
+        dash.dash_attn_bwd_prepare(o, x["do"], lse, tuple(x["q"].shape), Hkv, int(causal), sched, ws)
+        dash.dash_attn_bwd_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, int(causal), sched, ws)
+        dash.dash_attn_bwd_check(ws)
+        if sched != dash.ATOMIC:
+            for a, b in zip(good, (dq, dk, dv)):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16))
