@@ -31,6 +31,11 @@ calibrated FETCH_SIZE + WRITE_SIZE of that kernel read from the committed
 rocprofv3 summary, reported only while that summary's kernel-source hash
 matches the current source.  The cpu_baseline object times the float64 oracle
 on a bounded sample of the same workload on the host cores.
+
+The headline workload is the largest configuration, the 16k full-mask layer
+(B=1 S=16384 Hq=Hkv=32 D=128).  Unless --config or --headline-only is given,
+the line also carries "workloads": the same per-schedule measurements, the
+roofline of the best schedule and det/atomic for each other configuration.
 """
 
 import argparse
@@ -72,7 +77,16 @@ CONFIGS = {
                           desc="long-sequence causal attention backward shaped like a 7B "
                                "Qwen-style layer: B=1 S=16384 Hq=28 Hkv=4 (GQA 7) D=128"),
 }
-DEFAULT_CONFIG = "llama8b_causal"
+# the headline workload: the largest of the five configurations (the 16k
+# full-mask layer, 1.1e13 FLOPs per step); every other one is summarised in
+# the same line under "workloads"
+DEFAULT_CONFIG = "long_full"
+OTHER_WORKLOADS = ("small_full", "llama8b_causal", "dit_full", "qwen7b_causal")
+
+# kv heads of the float64 oracle's timed sample per workload (whole key/value
+# groups, so that dK/dV of those heads are complete): the first and last
+# groups of batch 0, about 10-20 s of host work on a 16-thread host
+CPU_SAMPLE_KV_HEADS = {"long_full": (0, 1, 2, 29, 30, 31), "qwen7b_causal": (0, 3)}
 
 
 def flops(cfg):
@@ -219,11 +233,13 @@ def committed_traffic(config, schedule):
     return float(m.group(1)) if m else None
 
 
-def cpu_baseline(cfg, budget_s=20.0):
-    """Time the float64 oracle on whole (batch, kv head) groups of the
-    workload until the budget is used or every group is done; report the
-    rate in TFLOP/s of the same FLOP formula.  Batch 0's inputs stand in for
-    every batch (the oracle's work does not depend on the values)."""
+def cpu_baseline(name, cfg, budget_s=20.0):
+    """Time the float64 oracle (forward + backward) on whole (batch, kv head)
+    groups of the workload and report the rate in TFLOP/s of the same FLOP
+    formula.  Workloads listed in CPU_SAMPLE_KV_HEADS time exactly those kv
+    heads of batch 0; the others take groups in order until the budget is
+    used or every group is done (batch 0's inputs stand in for every batch:
+    the oracle's work does not depend on the values)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import attention as oa
@@ -233,28 +249,50 @@ def cpu_baseline(cfg, budget_s=20.0):
     G = Hq // Hkv
     x = make_inputs(1, S, Hq, Hkv, D, seed=1000)
     h = {k: as_float64(v) for k, v in x.items()}
+    fixed = CPU_SAMPLE_KV_HEADS.get(name)
+    done = []
     t0 = time.perf_counter()
-    groups = 0
     while True:
-        kv = groups % Hkv
+        kv = fixed[len(done)] if fixed else len(done) % Hkv
         hs = list(range(kv * G, (kv + 1) * G))
         oa.attention_backward(h["q"][:, :, hs], h["k"][:, :, kv:kv + 1],
                               h["v"][:, :, kv:kv + 1], h["do"][:, :, hs], cfg["causal"])
-        groups += 1
-        if time.perf_counter() - t0 >= budget_s or groups >= B * Hkv:
+        done.append(kv)
+        if fixed:
+            if len(done) == len(fixed):
+                break
+        elif time.perf_counter() - t0 >= budget_s or len(done) >= B * Hkv:
             break
     dt = time.perf_counter() - t0
-    fl = flops(dict(cfg, B=1, Hq=G * groups))
+    fl = flops(dict(cfg, B=1, Hq=G * len(done)))
     threads = 0
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, info.get("num_threads", 0))
+    heads = sorted(g for kv in set(done) for g in range(kv * G, (kv + 1) * G))
+    if fixed:
+        what = ("the fixed sample of kv heads %s of batch 0 (query heads %s), %d of the "
+                "workload's %d (batch, kv head) groups"
+                % (list(fixed), _ranges(heads), len(done), B * Hkv))
+    else:
+        what = ("%d of %d (batch, kv head) groups (%d query heads; batch 0's inputs for every "
+                "batch)" % (len(done), B * Hkv, G * len(done)))
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
-            "sample": "float64 oracle forward+backward of %d of %d (batch, kv head) groups "
-                      "(%d query heads; batch 0's inputs for every batch) at S=%d D=%d, %.1f s; "
-                      "includes the oracle's own float64 forward"
-                      % (groups, B * Hkv, G * groups, S, D, dt)}
+            "sample": "float64 oracle forward+backward of %s at S=%d D=%d, %.1f s; the rate "
+                      "extrapolates linearly to the whole workload (heads are independent); "
+                      "includes the oracle's own float64 forward" % (what, S, D, dt)}
+
+
+def _ranges(xs):
+    out, i = [], 0
+    while i < len(xs):
+        j = i
+        while j + 1 < len(xs) and xs[j + 1] == xs[j] + 1:
+            j += 1
+        out.append(str(xs[i]) if i == j else "%d-%d" % (xs[i], xs[j]))
+        i = j + 1
+    return ",".join(out)
 
 
 def roofline(cfg, T, fl, kernel_ms, schedule, traffic):
@@ -320,6 +358,8 @@ def main():
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
     ap.add_argument("--schedules", default="naive,descending_q,shift,symmetric_shift,atomic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload, not the summary of the others")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference "
@@ -338,7 +378,6 @@ def main():
 
     import torch
     import scheduling_persistent_attn_amd as dash
-    from scheduling_persistent_attn_amd.inputs import make_inputs
 
     if args.copy_calibration:
         n = 1 << 30
@@ -361,28 +400,50 @@ def main():
               flush=True)
         return
 
-    cfg = CONFIGS[args.config]
+    head = measure(dash, args.config, args, headline=True)
+    line = head
+    if not args.headline_only and args.config == DEFAULT_CONFIG:
+        # every other workload in the same line: per-schedule whole-step and
+        # kernel rates, the roofline of its best schedule and det/atomic
+        line["workloads"] = {}
+        for name in OTHER_WORKLOADS:
+            w = measure(dash, name, args, headline=False)
+            line["workloads"][name] = w
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config, CONFIGS[args.config], args.cpu_budget)
+        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 6)
+    print(json.dumps(line), flush=True)
+
+
+def measure(dash, name, args, headline):
+    """Times every schedule of one workload.  headline=True returns the
+    benchmark line's fields; otherwise a summary of the workload."""
+    import torch
+    from scheduling_persistent_attn_amd.inputs import make_inputs
+
+    cfg = CONFIGS[name]
     B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
     T = dash.dash_attn_tile_size(S, D)
     N = (S + T - 1) // T
+    log("workload %s: %s" % (name, cfg["desc"]))
     x = make_inputs(B, S, Hq, Hkv, D, seed=1000, device="cuda")
     o, lse = dash.forward(x["q"], x["k"], x["v"], cfg["causal"])
     torch.cuda.synchronize()
     fl = flops(cfg)
 
     results = {}
-    for name in args.schedules.split(","):
-        sched = dash.SCHEDULES[name]
+    for sname in args.schedules.split(","):
+        sched = dash.SCHEDULES[sname]
         if sched == dash.SYMMETRIC_SHIFT and (not cfg["causal"] or N % 2):
             continue
         r = time_schedule(dash, x, o, lse, cfg, sched, args.steps, args.warmup)
         r["tflops"] = fl / (r["ms_mean"] * 1e-3) / 1e12
         r["kernel_tflops"] = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
         r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
-        results[name] = r
+        results[sname] = r
         rep = r.get("repro")
-        log("%-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak  (kernel %.3f ms)  waiting %4.1f%%%s"
-            % (name, r["ms_mean"], r["tflops"], r["pct_peak"], r["kernel_ms_mean"],
+        log("  %-16s %8.3f ms  %7.1f TFLOP/s  %5.1f%% of peak  (kernel %.3f ms)  waiting %4.1f%%%s"
+            % (sname, r["ms_mean"], r["tflops"], r["pct_peak"], r["kernel_ms_mean"],
                100.0 * r["wait_fraction"],
                "  %d of %d runs differ from the first" % (rep["differ"], rep["runs"]) if rep else ""))
     det = {k: v for k, v in results.items() if k != "atomic"}
@@ -390,8 +451,27 @@ def main():
     atomic = results.get("atomic")
     for k, v in results.items():
         v["det_over_atomic"] = (v["tflops"] / atomic["tflops"]) if atomic else None
-
     bestr = det[best]
+    sched_out = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                 for k, v in results.items()}
+    roof = roofline(cfg, T, fl, bestr["kernel_ms_mean"], best, committed_traffic(name, best))
+    bit_identical = (all(v["repro"]["differ"] == 0 for v in det.values())
+                     if all("repro" in v for v in det.values()) else None)
+    names = {v: k for k, v in dash.SCHEDULES.items()}
+    auto = names[dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, 1 if cfg["causal"] else 0)]
+    shape = {"B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
+             "mask": "causal" if cfg["causal"] else "full", "tile": T}
+    if not headline:
+        del x, o, lse
+        torch.cuda.empty_cache()
+        return dict(shape, workload=cfg["desc"], best_schedule=best,
+                    value=round(bestr["tflops"], 3), ms_per_step=round(bestr["ms_mean"], 4),
+                    pct_peak=round(bestr["pct_peak"], 2),
+                    det_over_atomic=round(bestr["det_over_atomic"], 4) if atomic else None,
+                    schedules=sched_out, roofline=roof,
+                    deterministic_bit_identical=bit_identical,
+                    auto_schedule=auto, auto_is_measured_best=auto == best)
+
     line = {
         "metric": "deterministic attn-bwd TFLOP/s on 1 MI355X; % bf16 MFMA peak; ratio vs atomic dQ",
         "value": round(bestr["tflops"], 3),
@@ -405,21 +485,24 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: N(0,1) fp32 cast to bf16, seeds 1000-1003; O and LSE from dash_attn_fwd",
-        "config": {"workload": cfg["desc"], "B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
-                   "mask": "causal" if cfg["causal"] else "full", "tile": T,
-                   "best_schedule": best},
+        "config": dict({"workload": cfg["desc"]}, **shape, best_schedule=best),
         "pct_peak": round(bestr["pct_peak"], 2),
         "det_over_atomic": round(bestr["det_over_atomic"], 4) if atomic else None,
-        "schedules": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
-                          for kk, vv in v.items()} for k, v in results.items()},
-        "roofline": roofline(cfg, T, fl, bestr["kernel_ms_mean"], best,
-                             committed_traffic(args.config, best)),
+        "schedules": sched_out,
+        "roofline": roof,
     }
     # run-to-run bit identity at this size, in this launch configuration:
     # every deterministic schedule must reproduce its first output exactly
     # (the atomic reference's count of differing runs is the positive control)
-    if all("repro" in v for v in det.values()):
-        line["deterministic_bit_identical"] = all(v["repro"]["differ"] == 0 for v in det.values())
+    if bit_identical is not None:
+        line["deterministic_bit_identical"] = bit_identical
+    # the shader clock the persistent kernel ran at (measured inside the last
+    # timed launch of the best schedule), beside the peak fraction, which is
+    # priced at the published 2.4 GHz
+    clk = bestr.get("sclk_mhz")
+    if clk:
+        line["sclk_mhz"] = clk
+        line["pct_peak_at_measured_clock"] = round(bestr["pct_peak"] * 2400.0 / clk, 2)
     # the whole attention layer: forward (O, LSE) then the backward step
     # above; forward FLOPs are 4*B*Hq*S^2*D (halved for a causal mask)
     fwd_ms = time_forward(dash, x, cfg, args.steps, args.warmup)
@@ -429,14 +512,11 @@ def main():
                      "tflops": round(1.4 * fl / (layer_ms * 1e-3) / 1e12, 3),
                      "fwd_tflops": round(0.4 * fl / (fwd_ms * 1e-3) / 1e12, 3)}
     # the schedule the simulator picks for this shape on this device (AUTO)
-    names = {v: k for k, v in dash.SCHEDULES.items()}
-    auto = names[dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, 1 if cfg["causal"] else 0)]
     line["auto_schedule"] = auto
     line["auto_is_measured_best"] = auto == best
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
-        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 6)
-    print(json.dumps(line), flush=True)
+    del x, o, lse
+    torch.cuda.empty_cache()
+    return line
 
 
 if __name__ == "__main__":

@@ -347,6 +347,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
 
   dash::FinParams& fp = P->fp;
   fp.dqacc = pp.dqacc;
+  fp.ctrl = pp.ctrl;
   fp.dq = dq;
   fp.B = B;
   fp.Hq = Hq;

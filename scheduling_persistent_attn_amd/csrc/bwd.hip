@@ -1001,6 +1001,9 @@ __global__ __launch_bounds__(256) void bwd_finalize(FinParams p) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)p.B * p.Hq * p.N * NP * NW * 16 * 64;
   if (idx >= total) return;
+  // a launch that drained on its error flag (watchdog, or a run without its
+  // prepare) leaves dq as it was
+  if (__hip_atomic_load(p.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
   const int lane = (int)(idx % 64);
   long long rest = idx / 64;
   const int r = (int)(rest % 16);

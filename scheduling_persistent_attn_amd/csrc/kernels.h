@@ -49,6 +49,7 @@ struct BwdParams {
 
 struct FinParams {
   const float* dqacc;
+  const int* ctrl;   // the error flag ctrl[1] up: write nothing
   void* dq;
   int B, Hq, S, N;
   float scale;
