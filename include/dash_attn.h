@@ -188,6 +188,25 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v,
                       int Hq, int Hkv, int S, int D, int mask, int schedule,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* dash_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * of the library, 64 MiB on each GPU the library runs on, held until the
+ * process ends; this call allocates nothing, and it clears what must start at
+ * zero with kernels (no memset nodes).  Same arguments (less the workspace),
+ * results, determinism contract and errors as dash_attn_bwd, plus
+ * DASH_ERR_WORKSPACE, before anything is enqueued, when the problem's
+ * workspace (dash_attn_bwd_workspace_size) exceeds 64 MiB.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one device race
+ * and give undefined results; order them with a stream or events.  The
+ * watchdog flag lands in the static array, where dash_attn_bwd_check cannot
+ * read it; callers that need it use dash_attn_bwd with a workspace of their
+ * own. */
+int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int S, int D, int mask, int schedule,
+                          void* stream);
+
 /* Waits for the stream, then reports DASH_ERR_NOT_PREPARED if the last
  * backward run on this workspace found it not prepared, DASH_ERR_TIMEOUT if
  * its watchdog fired, DASH_ERR_HIP on a runtime error, else DASH_OK.  Reads

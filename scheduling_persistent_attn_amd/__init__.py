@@ -34,7 +34,11 @@ SYMBOLS = (
     "dash_attn_bwd_grid_size", "dash_schedule_num_items",
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
     "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog", "dash_attn_bwd_wait_stats",
+    "dash_attn_bwd_noalloc",
 )
+
+# bytes of the static device workspace behind dash_attn_bwd_noalloc
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class DashError(RuntimeError):
@@ -78,6 +82,8 @@ def lib():
     L.dash_attn_bwd_prepare.restype = i
     L.dash_attn_bwd_run.argtypes = [p] * 7 + [i] * 7 + [p, sz, p]
     L.dash_attn_bwd_run.restype = i
+    L.dash_attn_bwd_noalloc.argtypes = [p] * 9 + [i] * 7 + [p]
+    L.dash_attn_bwd_noalloc.restype = i
     L.dash_attn_bwd_check.argtypes = [p, p]
     L.dash_attn_bwd_check.restype = i
     L.dash_attn_set_watchdog.argtypes = [d]
@@ -313,6 +319,25 @@ def dash_attn_bwd_run(q, k, v, dout, dq, dk, dv, mask, schedule, workspace, stre
                                  _stream(stream))
     if st != DASH_OK:
         raise DashError(st, "dash_attn_bwd_run")
+
+
+def dash_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, stream=None):
+    """dash_attn_bwd on the library's static device workspace (no workspace
+    argument; the library allocates nothing).  Problems whose workspace
+    exceeds NOALLOC_WORKSPACE_BYTES raise DashError (DASH_ERR_WORKSPACE)."""
+    import torch
+    _check_tensors([("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)], torch.bfloat16)
+    _check_tensors([("lse", lse)], torch.float32)
+    dims = _dims(q, k)
+    _check_layout(dims, [("q", q), ("o", o), ("dout", dout), ("dq", dq)],
+                  [("k", k), ("v", v), ("dk", dk), ("dv", dv)], [("lse", lse)])
+    B, S, Hq, Hkv, D = dims
+    st = lib().dash_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(mask),
+                                     int(schedule), _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd_noalloc")
 
 
 def dash_attn_bwd_check(workspace, stream=None):

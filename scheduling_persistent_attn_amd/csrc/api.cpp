@@ -407,6 +407,28 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v, const void* d
   return launch_main_phase(P, D, mask, (hipStream_t)stream);
 }
 
+int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int S, int D, int mask, int schedule,
+                          void* stream) {
+  int st = check_shape(B, Hq, Hkv, S, D, mask, schedule);
+  if (st != DASH_OK) return st;
+  Layout L;
+  st = make_layout(B, Hq, S, D, &L);
+  if (st != DASH_OK) return st;
+  // the static workspace is fixed in size: larger problems are refused
+  // before anything touches the device
+  if (L.total > dash::kScratchBytes) return DASH_ERR_WORKSPACE;
+  // an empty problem launches nothing and never looks at the workspace
+  if (B == 0 || S == 0)
+    return dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule,
+                         nullptr, 0, stream);
+  void* ws = nullptr;
+  if (dash::scratch_workspace(&ws) != hipSuccess) return DASH_ERR_HIP;
+  return dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule, ws,
+                       dash::kScratchBytes, stream);
+}
+
 int dash_attn_bwd_check(const void* workspace, void* stream) {
   if (!workspace) return DASH_ERR_NULL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;

@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "lds_layout.h"
 #include "schedule.h"
@@ -1021,6 +1023,37 @@ __global__ __launch_bounds__(256) void bwd_finalize(FinParams p) {
   if (row < p.S)
     ((bf16*)p.dq)[((size_t)((size_t)b * p.S + row) * p.Hq + h) * D + 32 * db + (lane & 31)] =
         (bf16)(p.dqacc[idx] * p.scale);
+}
+
+// ---------------------------------------------------------------------------
+// The workspace of dash_attn_bwd_noalloc: a file-scope device array, one copy
+// per GPU, held from the library's load until the process ends.  Host code
+// never uses the array's name as an address: its device address is looked up
+// once per device with hipGetSymbolAddress (with that device current) and
+// kept, and only that address is passed to kernels.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t scratch_workspace(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -65,6 +65,13 @@ struct FwdParams {
   float scale_log2e;
 };
 
+// Bytes of the static device workspace behind dash_attn_bwd_noalloc.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+
+// Device address of this GPU's static workspace (looked up once per device,
+// on the current device).
+hipError_t scratch_workspace(void** out);
+
 // Persistent workgroups per compute unit for the backward kernel of (D, T,
 // causal); 0 if not instantiated.
 int bwd_blocks_per_cu(int D, int T, bool causal);
