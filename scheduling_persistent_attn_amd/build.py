@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdash_attn.so")
-SOURCES = ["bwd.hip", "fwd.hip", "api.cpp", "sim.cpp"]
+SOURCES = ["bwd.hip", "bwd_wide.hip", "fwd.hip", "api.cpp", "sim.cpp"]
 HOST_ONLY = {"sim.cpp"}  # plain C++, no HIP
 ARCH = "gfx950"
 
@@ -33,7 +33,8 @@ COMMON = [
 # accumulators in the vector registers (the softmax reads S and dP and the
 # dQ partial sum is loaded straight into its accumulator), and pins the
 # operands it holds for a whole KV tile to the accumulation registers itself
-EXTRA = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "bwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

@@ -24,6 +24,7 @@ struct DeviceInfo {
   int cus = 0;
   long long wall_khz = 0;
   int bpc[2][2][2] = {};  // [D==128][T==128][causal] resident blocks per CU
+  int bpc_wide[2] = {};   // [causal] of the 256-key tile kernel
 };
 
 DeviceInfo g_dev[kMaxDevices];
@@ -47,6 +48,7 @@ int device_info(DeviceInfo** out) {
       for (int causal = 0; causal < 2; ++causal)
         d.bpc[cfg[0] == 128][cfg[1] == 128][causal] =
             dash::bwd_blocks_per_cu(cfg[0], cfg[1], causal != 0);
+    for (int causal = 0; causal < 2; ++causal) d.bpc_wide[causal] = dash::bwd_wide_blocks_per_cu(causal != 0);
     d.ready = true;
   }
   *out = &d;
@@ -54,6 +56,16 @@ int device_info(DeviceInfo** out) {
 }
 
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Persistent workgroups the backward kernel for tile T runs per compute unit.
+int blocks_per_cu(const DeviceInfo& d, int D, int T, int mask) {
+  if (T == 256) return d.bpc_wide[mask];
+  return d.bpc[D == 128][T == 128][mask];
+}
+
+// Turn counters per dQ tile: one per slice a wave reduces per pass -- 32 rows
+// x 32 features for tiles of 64 and 128, 32 rows x 16 features for 256.
+int slices_per_tile(int T, int D) { return T == 256 ? T * D / 512 : T * D / 1024; }
 
 struct Layout {
   int T = 0, N = 0, NW = 0;
@@ -77,8 +89,7 @@ int make_layout(int B, int Hq, int S, int D, Layout* L) {
   L->T = dash_attn_tile_size(S, D);
   if (L->T == 0) return DASH_ERR_UNSUPPORTED;
   L->N = (S + L->T - 1) / L->T;
-  // one turn counter per 32x32 slice of a dQ tile: T*D/1024 per tile
-  L->NW = L->T * D / 1024;
+  L->NW = slices_per_tile(L->T, D);
   const long long rows = (long long)B * Hq * L->N * L->T;
   L->n_rows = rows;
   L->n_counters = (long long)B * Hq * L->N * L->NW;
@@ -140,7 +151,7 @@ int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
       *out = e.schedule;
       return DASH_OK;
     }
-  const int grid = dev->cus * dev->bpc[D == 128][L.T == 128][mask];
+  const int grid = dev->cus * blocks_per_cu(*dev, D, L.T, mask);
   if (grid <= 0) return DASH_ERR_HIP;
   int sched = -1;
   st = dash_sim_select(mask, L.N, Hq / Hkv, B * Hkv, grid, 1, kAutoC, kAutoCDiag, kAutoR, &sched,
@@ -174,7 +185,7 @@ int dash_attn_bwd_auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask) 
 
 int dash_attn_tile_size(int S, int D) {
   if (D == 64) return S <= 512 ? 64 : 128;
-  if (D == 128) return 128;
+  if (D == 128) return S <= 512 ? 128 : 256;
   return 0;
 }
 
@@ -206,7 +217,7 @@ int dash_attn_bwd_grid_size(int S, int D, int mask) {
   if (T == 0 || (mask != 0 && mask != 1)) return 0;
   DeviceInfo* d = nullptr;
   if (device_info(&d) != DASH_OK) return 0;
-  return d->cus * d->bpc[D == 128][T == 128][mask];
+  return d->cus * blocks_per_cu(*d, D, T, mask);
 }
 
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -286,8 +297,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   DeviceInfo* dev = nullptr;
   st = device_info(&dev);
   if (st != DASH_OK) return st;
-  const int bpc = dev->bpc[D == 128][L.T == 128][mask];
-  const int grid = dev->cus * bpc;
+  const int grid = dev->cus * blocks_per_cu(*dev, D, L.T, mask);
   if (grid <= 0) return DASH_ERR_HIP;
   const int G = Hq / Hkv;
   const int ipg = dash::items_per_group(mask, schedule, L.N);
@@ -358,8 +368,14 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
 }
 
 int launch_main_phase(const BwdPlan& P, int D, int mask, hipStream_t s) {
-  if (dash::launch_bwd_main(D, P.L.T, mask == DASH_MASK_CAUSAL, P.bp, P.grid, s) != hipSuccess)
-    return DASH_ERR_HIP;
+  const bool causal = mask == DASH_MASK_CAUSAL;
+  if (P.L.T == 256) {
+    if (dash::launch_bwd_wide(causal, P.bp, P.grid, s) != hipSuccess) return DASH_ERR_HIP;
+    if (P.bp.schedule == DASH_SCHED_ATOMIC && dash::launch_finalize_wide(P.fp, s) != hipSuccess)
+      return DASH_ERR_HIP;
+    return DASH_OK;
+  }
+  if (dash::launch_bwd_main(D, P.L.T, causal, P.bp, P.grid, s) != hipSuccess) return DASH_ERR_HIP;
   if (P.bp.schedule == DASH_SCHED_ATOMIC &&
       dash::launch_finalize_atomic(D, P.L.T, P.fp, s) != hipSuccess)
     return DASH_ERR_HIP;

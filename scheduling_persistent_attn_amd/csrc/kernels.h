@@ -77,6 +77,11 @@ hipError_t scratch_workspace(void** out);
 int bwd_blocks_per_cu(int D, int T, bool causal);
 int bwd_block_threads(int T);
 
+// The 256-key tile kernel (head dim 128; bwd_wide.hip).
+int bwd_wide_blocks_per_cu(bool causal);
+hipError_t launch_bwd_wide(bool causal, const BwdParams& p, int grid, hipStream_t s);
+hipError_t launch_finalize_wide(const FinParams& p, hipStream_t s);
+
 hipError_t launch_preprocess(const PreParams& p, hipStream_t s);
 hipError_t launch_bwd_main(int D, int T, bool causal, const BwdParams& p, int grid,
                            hipStream_t s);

@@ -57,10 +57,16 @@ def contributors(causal, N, j):
     return j + 1 if causal else N
 
 
+def slices_per_tile(T, D):
+    """Turn counters per dQ tile: one per slice a wave reduces per pass (32 x
+    32 for tiles of 64 and 128 rows, 32 x 16 for 256)."""
+    return T * D // 512 if T == 256 else T * D // 1024
+
+
 def expected_counters(B, Hq, S, D, causal):
     T = dash.dash_attn_tile_size(S, D)
     N = (S + T - 1) // T
-    NW = T * D // 1024  # one counter per 32x32 slice of a dQ tile
+    NW = slices_per_tile(T, D)
     want = np.zeros((B, Hq, N, NW), dtype=np.int64)
     for j in range(N):
         want[:, :, j, :] = contributors(causal, N, j)
@@ -70,7 +76,7 @@ def expected_counters(B, Hq, S, D, causal):
 def read_counters(workspace, B, Hq, S, D):
     T = dash.dash_attn_tile_size(S, D)
     N = (S + T - 1) // T
-    NW = T * D // 1024  # one counter per 32x32 slice of a dQ tile
+    NW = slices_per_tile(T, D)
     n = B * Hq * N * NW
     # after the 64 control words and the 4096 x 4 uint64 wait counters
     off = (256 + 4096 * 32) // 4

@@ -68,16 +68,22 @@ def test_status_strings():
 def test_tile_and_workspace_size():
     assert dash.dash_attn_tile_size(256, 64) == 64
     assert dash.dash_attn_tile_size(4096, 64) == 128
-    assert dash.dash_attn_tile_size(4096, 128) == 128
+    assert dash.dash_attn_tile_size(512, 128) == 128
+    assert dash.dash_attn_tile_size(513, 128) == 256
+    assert dash.dash_attn_tile_size(4096, 128) == 256
     assert dash.dash_attn_tile_size(100, 96) == 0
-    B, Hq, Hkv, S, D = 4, 32, 8, 4096, 128
-    T, N = 128, 32
-    n = dash.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, 1, 2)
-    rows = B * Hq * N * T
-    # control words, wait counters (4096 x 4 uint64), turn counters, the two
-    # per-row arrays and the fp32 dQ partial sums
-    want = 256 + 4096 * 32 + B * Hq * N * (T * D // 1024) * 4 + 2 * rows * 4 + rows * D * 4
-    assert want <= n <= want + 5 * 256
+    # one turn counter per slice a wave reduces per pass: 32 x 32 for tiles of
+    # 64 and 128, 32 x 16 for 256
+    for (B, Hq, Hkv, S, D, T, per_tile) in ((4, 32, 8, 4096, 128, 256, 256 * 128 // 512),
+                                            (2, 8, 4, 512, 128, 128, 128 * 128 // 1024),
+                                            (2, 24, 24, 4096, 64, 128, 128 * 64 // 1024)):
+        N = (S + T - 1) // T
+        n = dash.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, 1, 2)
+        rows = B * Hq * N * T
+        # control words, wait counters (4096 x 4 uint64), turn counters, the two
+        # per-row arrays and the fp32 dQ partial sums
+        want = 256 + 4096 * 32 + B * Hq * N * per_tile * 4 + 2 * rows * 4 + rows * D * 4
+        assert want <= n <= want + 5 * 256, (S, D)
     # ragged S rounds up to whole tiles
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 300, 64, 0, 0) > 0
     # invalid
@@ -303,9 +309,9 @@ def test_sim_report_closed_forms(capsys):
     """bench.py --sim-report on the large workloads; two cases have closed
     forms.  dit_full at P = 256, r = 0: 48 groups x 32 chains of 32 unit tasks
     on 256 workers are 6 rounds of 32, so every schedule's critical path is 192.
-    llama8b_causal, symmetric shift, P = 256, r = 0: 32 groups x 16 pairs of
-    33 tasks for each of 4 query heads (132 per item) in 2 rounds: 264, with
-    efficiency 1 and no Lemma 1 violation."""
+    llama8b_causal, symmetric shift, P = 256, r = 0, with 256-key tiles (N =
+    16): 32 groups x 8 pairs of 17 tasks for each of 4 query heads (68 per
+    item) in one round: 68, with efficiency 1 and no Lemma 1 violation."""
     import json
     sys.path.insert(0, str(ROOT))
     import bench
@@ -316,7 +322,8 @@ def test_sim_report_closed_forms(capsys):
     for s in ("naive", "descending_q", "shift"):
         assert pick[("dit_full", 256, 0.0, s)]["critical_path"] == 192.0
     sym = pick[("llama8b_causal", 256, 0.0, "symmetric_shift")]
-    assert sym["critical_path"] == 264.0 and sym["lemma1_violations"] == 0
+    assert dash.dash_attn_tile_size(4096, 128) == 256
+    assert sym["critical_path"] == 68.0 and sym["lemma1_violations"] == 0
     assert abs(sym["efficiency"] - 1.0) < 1e-12
     assert not any(r["deadlock"] for r in rows)
 

@@ -38,6 +38,11 @@ CASES = [
     (1, 64, 1, 1, 128, False),    # single partial tile
     (2, 512, 8, 4, 64, True),     # 8 (batch, kv head) groups: one item queue per XCD
     (2, 512, 8, 4, 128, False),
+    (1, 1024, 4, 2, 128, True),   # 256-key tiles: N = 4, GQA groups of 2
+    (1, 1100, 2, 1, 128, False),  # 256-key tiles, partial last tile (N = 5)
+    (2, 768, 4, 4, 128, True),    # 256-key tiles, N = 3 (no symmetric shift)
+    (1, 2048, 2, 2, 128, True),   # 256-key tiles, N = 8
+    (1, 700, 3, 1, 128, True),    # 256-key tiles, partial last tile, G = 3
 ]
 
 
