@@ -95,9 +95,11 @@ def flops(cfg):
     return f / 2 if cfg["causal"] else f
 
 
-def algorithmic_bytes(cfg, T):
+def algorithmic_bytes(cfg, T, parts=1):
     """Bytes one backward launch must move between HBM and the chip under
-    this design (whole tiles; see the module docstring)."""
+    this design (whole tiles; see the module docstring).  With the query heads
+    split into `parts`, every part loads K and V itself and writes fp32 dK/dV
+    sums that the final pass reads back."""
     B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
     N = (S + T - 1) // T
     tiles = B * Hq * N                                     # dQ tiles
@@ -105,7 +107,10 @@ def algorithmic_bytes(cfg, T):
     per_task = 2 * T * D * 2 + 2 * T * 4                   # Q, dO tiles; -lse/scale, -Dl
     handoff = 2 * (tasks - tiles) * T * D * 4              # fp32 partial sum: load + store
     dq_out = tiles * T * D * 2
-    kv = B * Hkv * N * 4 * T * D * 2                       # K, V in; dK, dV out
+    kv_tiles = B * Hkv * N
+    kv = kv_tiles * (parts * 2 * T * D * 2 + 2 * T * D * 2)  # K, V in (per part); dK, dV out
+    if parts > 1:
+        kv += kv_tiles * parts * 2 * T * D * 4 * 2           # fp32 part sums: store + load
     return tasks * per_task + handoff + dq_out + kv
 
 
@@ -296,10 +301,10 @@ def _ranges(xs):
     return ",".join(out)
 
 
-def roofline(cfg, T, fl, kernel_ms, schedule, traffic):
+def roofline(cfg, T, fl, kernel_ms, schedule, traffic, parts=1):
     """The persistent kernel against the peak its algorithmic intensity
     selects (ridge = PEAK_BF16 / PEAK_HBM FLOP per byte)."""
-    nbytes = algorithmic_bytes(cfg, T)
+    nbytes = algorithmic_bytes(cfg, T, parts)
     gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     tflops = fl / (kernel_ms * 1e-3) / 1e12
     intensity = fl / nbytes
@@ -455,13 +460,15 @@ def measure(dash, name, args, headline):
     bestr = det[best]
     sched_out = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  for k, v in results.items()}
-    roof = roofline(cfg, T, fl, bestr["kernel_ms_mean"], best, committed_traffic(name, best))
+    mask = 1 if cfg["causal"] else 0
+    parts = dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, mask, dash.SCHEDULES[best])
+    roof = roofline(cfg, T, fl, bestr["kernel_ms_mean"], best, committed_traffic(name, best), parts)
     bit_identical = (all(v["repro"]["differ"] == 0 for v in det.values())
                      if all("repro" in v for v in det.values()) else None)
     names = {v: k for k, v in dash.SCHEDULES.items()}
     auto = names[dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, 1 if cfg["causal"] else 0)]
     shape = {"B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
-             "mask": "causal" if cfg["causal"] else "full", "tile": T}
+             "mask": "causal" if cfg["causal"] else "full", "tile": T, "head_parts": parts}
     if not headline:
         del x, o, lse
         torch.cuda.empty_cache()

@@ -98,9 +98,24 @@ enum dash_status {
 };
 
 /* Query-tile and key/value-tile edge T used for a problem (both sides use the
- * same T): 64 when D == 64 and S <= 512, else 128.  Returns 0 if D is
- * unsupported. */
+ * same T): for D == 64, 64 when S <= 512, else 128; for D == 128, 128 when
+ * S <= 512, else 256 (a unit then holds the dK/dV of 256 keys, which halves
+ * the bytes moved per FLOP).  Returns 0 if D is unsupported. */
 int dash_attn_tile_size(int S, int D);
+
+/* Number of parts the query heads of each (batch, key/value head) group are
+ * split into, a function of the arguments alone (0 if invalid).  Normally 1:
+ * one item serves a key/value tile (or symmetric pair) for all G = Hq/Hkv
+ * query heads, so dK/dV are summed in registers.  With 256-key tiles a launch
+ * can have fewer items than an MI355X has compute units (256); then the heads
+ * are split into `parts` runs of G/parts consecutive heads -- the smallest
+ * divisor of G that gives at least 256 items, else G -- and every item
+ * exists once per part, serving only that part's heads.  Items are dispatched
+ * group by group, part by part, so the items of one part run together (the
+ * shift family needs that).  Each part writes its fp32 dK/dV to the workspace
+ * and a final pass sums the parts in ascending order.  For AUTO, the largest
+ * over the schedules it can resolve to. */
+int dash_attn_bwd_head_parts(int B, int Hq, int Hkv, int S, int D, int mask, int schedule);
 
 /* Bytes of workspace dash_attn_bwd needs for these arguments, or 0 if the
  * arguments are invalid.  Layout (offsets rounded up to 256 bytes):
@@ -113,13 +128,17 @@ int dash_attn_tile_size(int S, int D);
  *             found the turn not yet taken: [0] count, [1] polls, [2]
  *             wall-clock ticks spent (dash_attn_bwd_wait_stats sums them)
  *   counters  B*Hq*N*W int32: the turn counter of every (batch, query head,
- *             dQ tile, slice) -- a slice is one 32-row x 32-feature block of
- *             the tile; after a deterministic backward each holds the number
- *             of key/value tiles that reduced into that dQ tile
- *             (N = ceil(S/T), W = T*D/1024)
+ *             dQ tile, slice) -- a slice is the block of the tile one wave
+ *             reduces per pass; after a deterministic backward each holds the
+ *             number of key/value tiles that reduced into that dQ tile
+ *             (N = ceil(S/T))
  *   delta     B*Hq*N*T fp32: -rowsum(dout * o), zero past S
  *   lse2      B*Hq*N*T fp32: -lse / scale, -inf past S
  *   dqacc     B*Hq*N*T*D fp32: dQ partial sums in the kernels' lane order
+ *   dkvp      only when the heads are split (dash_attn_bwd_head_parts > 1):
+ *             2*B*Hkv*parts*N*T*D fp32, each part's dK then dV sums
+ * (W = T*D/1024 for tiles of 64 and 128: one counter per 32 x 32 slice; W =
+ * T*D/512 for 256: one per 32 x 16 slice.)
  */
 size_t dash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int S, int D,
                                     int mask, int schedule);
@@ -144,7 +163,9 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * streams and timing.  Different schedules may differ in the last bits.
  * dK/dV of a key/value tile are summed over its query heads inside one unit,
  * in the unit's fixed task order (each query tile of the walk taken for all
- * heads in turn).  The dQ tile j of query head h is reduced in the order given
+ * heads in turn); when the heads are split into parts (see
+ * dash_attn_bwd_head_parts) each part is summed that way and the parts are
+ * then added in ascending order.  The dQ tile j of query head h is reduced in the order given
  * by the schedule (see enum dash_schedule) using per-tile turn counters in
  * the workspace.
  *

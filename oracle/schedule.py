@@ -103,12 +103,22 @@ def symmetric_pair_parts(N, p):
     return ph1, ph2a, ph2b
 
 
-def items(schedule, mask, N, G=1):
+def items(schedule, mask, N, G=1, parts=1):
     """Items of one (batch, KV head) group, in dispatch order.
 
     Each item is a list of tasks (g, i, j): query head g of the group, KV
-    tile i, Q tile j.
+    tile i, Q tile j.  With parts > 1 (a divisor of G) the query heads are
+    split into `parts` consecutive runs of G / parts heads, and each part has
+    its own copy of every item, serving only its heads; the parts follow one
+    another in dispatch order (part 0's items first).  dK/dV of a key/value
+    tile are then the sum of the parts' sums, added in ascending part order.
     """
+    if parts != 1:
+        if parts < 1 or G % parts:
+            raise ValueError("parts must divide G")
+        Gp = G // parts
+        return [[(k * Gp + g, i, j) for (g, i, j) in it]
+                for k in range(parts) for it in items(schedule, mask, N, Gp)]
     out = []
     # the atomic reference's result does not depend on its order; on causal
     # masks with an even tile count it takes the symmetric pairs (the

@@ -34,7 +34,7 @@ SYMBOLS = (
     "dash_attn_bwd_grid_size", "dash_schedule_num_items",
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
     "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog", "dash_attn_bwd_wait_stats",
-    "dash_attn_bwd_noalloc",
+    "dash_attn_bwd_noalloc", "dash_attn_bwd_head_parts",
 )
 
 # bytes of the static device workspace behind dash_attn_bwd_noalloc
@@ -82,6 +82,8 @@ def lib():
     L.dash_attn_bwd_prepare.restype = i
     L.dash_attn_bwd_run.argtypes = [p] * 7 + [i] * 7 + [p, sz, p]
     L.dash_attn_bwd_run.restype = i
+    L.dash_attn_bwd_head_parts.argtypes = [i] * 7
+    L.dash_attn_bwd_head_parts.restype = i
     L.dash_attn_bwd_noalloc.argtypes = [p] * 9 + [i] * 7 + [p]
     L.dash_attn_bwd_noalloc.restype = i
     L.dash_attn_bwd_check.argtypes = [p, p]
@@ -125,6 +127,10 @@ def dash_attn_tile_size(S, D):
 
 def dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, mask, schedule):
     return lib().dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, mask, schedule)
+
+
+def dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, mask, schedule):
+    return lib().dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, int(mask), int(schedule))
 
 
 def dash_attn_bwd_grid_size(S, D, mask):

@@ -68,9 +68,9 @@ int blocks_per_cu(const DeviceInfo& d, int D, int T, int mask) {
 int slices_per_tile(int T, int D) { return T == 256 ? T * D / 512 : T * D / 1024; }
 
 struct Layout {
-  int T = 0, N = 0, NW = 0;
-  size_t ctrl = 0, waits = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, total = 0;
-  long long n_counters = 0, n_rows = 0, n_dqacc = 0;
+  int T = 0, N = 0, NW = 0, parts = 1;
+  size_t ctrl = 0, waits = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, dkvp = 0, total = 0;
+  long long n_counters = 0, n_rows = 0, n_dqacc = 0, n_dkvp = 0;
 };
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -85,10 +85,37 @@ int check_shape(int B, int Hq, int Hkv, int S, int D, int mask, int schedule) {
   return DASH_OK;
 }
 
-int make_layout(int B, int Hq, int S, int D, Layout* L) {
+// A launch with fewer items than this leaves compute units of an MI355X idle
+// (256 compute units; the 256-key tile kernel runs one workgroup on each).
+constexpr int kSplitTargetItems = 256;
+
+// Query-head parts per base item, a function of the shape alone: with 256-key
+// tiles and grouped heads, the smallest divisor d of G for which the launch
+// has at least kSplitTargetItems items, else G; 1 otherwise.  For AUTO, the
+// largest over the schedules it can resolve to (the workspace then covers
+// any of them).
+int head_parts(int B, int Hkv, int G, int N, int T, int mask, int schedule) {
+  if (T != 256 || G == 1 || N == 0) return 1;
+  if (schedule == DASH_SCHED_AUTO) {
+    int m = 1;
+    for (int s = DASH_SCHED_NAIVE; s <= DASH_SCHED_SYMMETRIC_SHIFT; ++s) {
+      if (s == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || N % 2 != 0)) continue;
+      const int d = head_parts(B, Hkv, G, N, T, mask, s);
+      m = d > m ? d : m;
+    }
+    return m;
+  }
+  const long long base = (long long)B * Hkv * dash::items_per_group(mask, schedule, N);
+  for (int d = 1; d <= G; ++d)
+    if (G % d == 0 && base * d >= kSplitTargetItems) return d;
+  return G;
+}
+
+int make_layout(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, Layout* L) {
   L->T = dash_attn_tile_size(S, D);
   if (L->T == 0) return DASH_ERR_UNSUPPORTED;
   L->N = (S + L->T - 1) / L->T;
+  L->parts = head_parts(B, Hkv, Hq / Hkv, L->N, L->T, mask, schedule);
   L->NW = slices_per_tile(L->T, D);
   const long long rows = (long long)B * Hq * L->N * L->T;
   L->n_rows = rows;
@@ -112,6 +139,10 @@ int make_layout(int B, int Hq, int S, int D, Layout* L) {
   off += round256((size_t)rows * sizeof(float));
   L->dqacc = off;
   off += round256((size_t)L->n_dqacc * sizeof(float));
+  // last, so that no other offset depends on the number of parts
+  L->dkvp = off;
+  L->n_dkvp = L->parts > 1 ? 2LL * B * Hkv * L->parts * L->N * L->T * D : 0;
+  off += round256((size_t)L->n_dkvp * sizeof(float));
   L->total = off;
   return DASH_OK;
 }
@@ -133,7 +164,7 @@ int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
   int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_NAIVE);
   if (st != DASH_OK) return st;
   Layout L;
-  st = make_layout(B, Hq, S, D, &L);
+  st = make_layout(B, Hq, Hkv, S, D, mask, DASH_SCHED_NAIVE, &L);
   if (st != DASH_OK) return st;
   if (B == 0 || S == 0) {
     *out = DASH_SCHED_NAIVE;
@@ -153,9 +184,35 @@ int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
     }
   const int grid = dev->cus * blocks_per_cu(*dev, D, L.T, mask);
   if (grid <= 0) return DASH_ERR_HIP;
+  // every deterministic schedule that applies, each with its own split of
+  // the query heads (a split group simulates as `parts` groups of G/parts
+  // heads, in the same dispatch order); the shortest critical path wins,
+  // ties to the earlier of SYMMETRIC_SHIFT, SHIFT, DESCENDING_Q, NAIVE
   int sched = -1;
-  st = dash_sim_select(mask, L.N, Hq / Hkv, B * Hkv, grid, 1, kAutoC, kAutoCDiag, kAutoR, &sched,
-                       nullptr);
+  {
+    static const int order[4] = {DASH_SCHED_SYMMETRIC_SHIFT, DASH_SCHED_SHIFT, DASH_SCHED_DESCENDING_Q,
+                                 DASH_SCHED_NAIVE};
+    const int G = Hq / Hkv;
+    double best = 0.0;
+    st = DASH_OK;
+    for (int s : order) {
+      if (s == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || L.N % 2 != 0)) continue;
+      const int parts = head_parts(B, Hkv, G, L.N, L.T, mask, s);
+      dash_sim_result res;
+      const int rs = dash_sim_run(mask, s, L.N, G / parts, B * Hkv * parts, grid, 1, kAutoC, kAutoCDiag,
+                                  kAutoR, &res);
+      if (rs != DASH_OK) {
+        st = rs;
+        break;
+      }
+      if (res.deadlock) continue;
+      if (sched < 0 || res.makespan < best) {
+        sched = s;
+        best = res.makespan;
+      }
+    }
+    if (st == DASH_OK && sched < 0) st = DASH_ERR_UNSUPPORTED;
+  }
   if (st == DASH_ERR_UNSUPPORTED || st == DASH_ERR_SCHEDULE_MASK) {
     // too large to simulate: the simulator's usual order on co-resident
     // groups, else the descending order (causal) or the naive one
@@ -183,6 +240,13 @@ int dash_attn_bwd_auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask) 
   return st == DASH_OK ? sched : -st;
 }
 
+int dash_attn_bwd_head_parts(int B, int Hq, int Hkv, int S, int D, int mask, int schedule) {
+  if (check_shape(B, Hq, Hkv, S, D, mask, schedule) != DASH_OK) return 0;
+  Layout L;
+  if (make_layout(B, Hq, Hkv, S, D, mask, schedule, &L) != DASH_OK) return 0;
+  return L.parts;
+}
+
 int dash_attn_tile_size(int S, int D) {
   if (D == 64) return S <= 512 ? 64 : 128;
   if (D == 128) return S <= 512 ? 128 : 256;
@@ -193,7 +257,7 @@ size_t dash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int S, int D, int ma
                                     int schedule) {
   if (check_shape(B, Hq, Hkv, S, D, mask, schedule) != DASH_OK) return 0;
   Layout L;
-  if (make_layout(B, Hq, S, D, &L) != DASH_OK) return 0;
+  if (make_layout(B, Hq, Hkv, S, D, mask, schedule, &L) != DASH_OK) return 0;
   return L.total;
 }
 
@@ -259,6 +323,7 @@ struct BwdPlan {
   dash::PreParams pp;
   dash::BwdParams bp;
   dash::FinParams fp;
+  dash::DkvFinParams kp;
 };
 
 // Validates the arguments of a backward and fills the launch parameters.
@@ -273,7 +338,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   int st = check_shape(B, Hq, Hkv, S, D, mask, schedule);
   if (st != DASH_OK) return st;
   Layout& L = P->L;
-  st = make_layout(B, Hq, S, D, &L);
+  st = make_layout(B, Hq, Hkv, S, D, mask, schedule, &L);
   if (st != DASH_OK) return st;
   if (schedule == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || (L.N % 2) != 0))
     return DASH_ERR_SCHEDULE_MASK;
@@ -293,6 +358,9 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (schedule == DASH_SCHED_AUTO) {
     st = auto_schedule(B, Hq, Hkv, S, D, mask, &schedule);
     if (st != DASH_OK) return st;
+    // the resolved schedule's layout: the same offsets, at most as many parts
+    st = make_layout(B, Hq, Hkv, S, D, mask, schedule, &L);
+    if (st != DASH_OK) return st;
   }
   DeviceInfo* dev = nullptr;
   st = device_info(&dev);
@@ -300,10 +368,11 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   const int grid = dev->cus * blocks_per_cu(*dev, D, L.T, mask);
   if (grid <= 0) return DASH_ERR_HIP;
   const int G = Hq / Hkv;
-  const int ipg = dash::items_per_group(mask, schedule, L.N);
+  const int base_items = dash::items_per_group(mask, schedule, L.N);
+  const int ipg = base_items * L.parts;
   // The shift family waits on chains that come later in the dispatch order,
-  // so a whole group of items must be able to run at once.
-  if ((schedule == DASH_SCHED_SHIFT || schedule == DASH_SCHED_SYMMETRIC_SHIFT) && ipg > grid)
+  // so the items of one part of a group must be able to run at once.
+  if ((schedule == DASH_SCHED_SHIFT || schedule == DASH_SCHED_SYMMETRIC_SHIFT) && base_items > grid)
     return DASH_ERR_UNSUPPORTED;
 
   char* ws = (char*)workspace;
@@ -350,10 +419,28 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   bp.schedule = schedule;
   bp.items_per_group = ipg;
   bp.total_items = B * Hkv * ipg;
+  bp.parts = L.parts;
+  bp.Gp = G / L.parts;
+  bp.base_items = base_items;
+  bp.dkv_part = L.parts > 1 ? (float*)(ws + L.dkvp) : nullptr;
+  bp.NT = L.N * L.T;
   bp.scale = (float)(1.0 / __builtin_sqrt((double)D));
   bp.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   bp.spin_ticks = g_watchdog_us.load() * dev->wall_khz / 1000;
   P->grid = grid < bp.total_items ? grid : bp.total_items;
+
+  dash::DkvFinParams& kp = P->kp;
+  kp.dkv_part = bp.dkv_part;
+  kp.dk = dk;
+  kp.dv = dv;
+  kp.ctrl = pp.ctrl;
+  kp.B = B;
+  kp.Hkv = Hkv;
+  kp.S = S;
+  kp.NT = bp.NT;
+  kp.D = D;
+  kp.parts = L.parts;
+  kp.scale = (float)(1.0 / __builtin_sqrt((double)D));
 
   dash::FinParams& fp = P->fp;
   fp.dqacc = pp.dqacc;
@@ -373,6 +460,7 @@ int launch_main_phase(const BwdPlan& P, int D, int mask, hipStream_t s) {
     if (dash::launch_bwd_wide(causal, P.bp, P.grid, s) != hipSuccess) return DASH_ERR_HIP;
     if (P.bp.schedule == DASH_SCHED_ATOMIC && dash::launch_finalize_wide(P.fp, s) != hipSuccess)
       return DASH_ERR_HIP;
+    if (P.L.parts > 1 && dash::launch_dkv_finalize(P.kp, s) != hipSuccess) return DASH_ERR_HIP;
     return DASH_OK;
   }
   if (dash::launch_bwd_main(D, P.L.T, causal, P.bp, P.grid, s) != hipSuccess) return DASH_ERR_HIP;
@@ -430,7 +518,7 @@ int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const voi
   int st = check_shape(B, Hq, Hkv, S, D, mask, schedule);
   if (st != DASH_OK) return st;
   Layout L;
-  st = make_layout(B, Hq, S, D, &L);
+  st = make_layout(B, Hq, Hkv, S, D, mask, schedule, &L);
   if (st != DASH_OK) return st;
   // the static workspace is fixed in size: larger problems are refused
   // before anything touches the device

@@ -395,17 +395,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
     const int grp = item / p.items_per_group;
     const int local = item - grp * p.items_per_group;
     const int b = grp / p.Hkv, hk = grp - b * p.Hkv;
-    const int len = item_len(mask, SCHED, N, G, local);
-    Task tn = task_at(mask, SCHED, N, G, local, 0);
-    stage_load<D, BQ, C::NW>(stage, p, T, b, hk * G + tn.g, tn.j, 0, true, voffQ, w, lane);
+    // this item's part of the group's query heads and its base item
+    const int part = local / p.base_items;
+    const int base = local - part * p.base_items;
+    const int Gp = p.Gp;
+    const int h0 = hk * G + part * Gp;  // first query head of the part
+    const int len = item_len(mask, SCHED, N, Gp, base);
+    Task tn = task_at(mask, SCHED, N, Gp, base, 0);
+    stage_load<D, BQ, C::NW>(stage, p, T, b, h0 + tn.g, tn.j, 0, true, voffQ, w, lane);
     stage_store<D, BQ, C::NW>(stage, smem + C::OFF_Q + (gp & 1) * C::Q_TILE, smem + C::OFF_DO + (gp & 1) * C::Q_TILE,
                               smem + C::OFF_LD + (gp & 1) * 2 * 4 * BQ, w, lane);
 
     for (int step = 0; step < len; ++step) {
       const Task t = tn;
-      const int i = t.i, j = t.j, h = hk * G + t.g;
+      const int i = t.i, j = t.j, h = h0 + t.g;
       const bool has_next = step + 1 < len;
-      if (has_next) tn = task_at(mask, SCHED, N, G, local, step + 1);
+      if (has_next) tn = task_at(mask, SCHED, N, Gp, base, step + 1);
       if (t.seg_begin) {
         // new KV tile: K into LDS, V rows of this wave's keys into registers
         __syncthreads();  // the K tile of the previous run is no longer read
@@ -470,7 +475,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
         const bool stage_next = hp + 1 < NP || has_next;
         {
           const bool same = hp + 1 < NP;
-          stage_load<D, BQ, C::NW>(stage, p, T, b, same ? h : hk * G + tn.g, same ? j : tn.j, same ? hp + 1 : 0,
+          stage_load<D, BQ, C::NW>(stage, p, T, b, same ? h : h0 + tn.g, same ? j : tn.j, same ? hp + 1 : 0,
                                    stage_next, voffQ, w, lane);
         }
         order_point();
@@ -544,7 +549,25 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
         sb = sb == 2 ? 0 : sb + 1;
       }
 
-      if (t.seg_end) {
+      if (t.seg_end && p.parts > 1) {
+        // this part's fp32 dK/dV of key/value tile i (unscaled), summed over
+        // the parts by bwd_dkv_finalize; rows past S are written too (the
+        // buffer is padded to whole tiles) and never read
+        const long long prow = ((long long)(b * p.Hkv + hk) * p.parts + part) * p.NT + i * T + key_local;
+        float* const pk = p.dkv_part + prow * D;
+        float* const pv = p.dkv_part + (long long)p.B * p.Hkv * p.parts * p.NT * D + prow * D;
+#pragma unroll
+        for (int md = 0; md < C::DB; ++md) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 xk = {dK[md][4 * q4], dK[md][4 * q4 + 1], dK[md][4 * q4 + 2], dK[md][4 * q4 + 3]};
+            const f32x4 xv = {dV[md][4 * q4], dV[md][4 * q4 + 1], dV[md][4 * q4 + 2], dV[md][4 * q4 + 3]};
+            const int d0 = 32 * md + 8 * q4 + 4 * hg;
+            *reinterpret_cast<f32x4*>(pk + d0) = xk;
+            *reinterpret_cast<f32x4*>(pv + d0) = xv;
+          }
+        }
+      } else if (t.seg_end) {
         // dK = scale * dS^T Q, dV = P^T dO of key/value tile i, bf16
         if (i * T + key_local < S) {
           const int off = ((b * S + i * T + key_local) * p.Hkv + hk) * D;
@@ -598,6 +621,42 @@ __global__ __launch_bounds__(256) void bwd_finalize_wide(FinParams p) {
         (bf16)(p.dqacc[idx] * p.scale);
 }
 
+// dK/dV of split groups: dk[b, s, hk, :] = scale * sum over the parts of
+// their fp32 partials, added in ascending part order (a fixed order, so the
+// result is reproducible), then rounded to bf16; dv likewise without the
+// scale.  One thread per four features.
+__global__ __launch_bounds__(256) void bwd_dkv_finalize(DkvFinParams p) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int q4n = p.D / 4;
+  const long long total = 2LL * p.B * p.Hkv * p.S * q4n;
+  if (idx >= total) return;
+  if (__hip_atomic_load(p.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+  const int q4 = (int)(idx % q4n);
+  long long rest = idx / q4n;
+  const int hk = (int)(rest % p.Hkv);
+  rest /= p.Hkv;
+  const int s = (int)(rest % p.S);
+  rest /= p.S;
+  const int b = (int)(rest % p.B);
+  const int which = (int)(rest / p.B);  // 0: dK, 1: dV
+  const long long half = (long long)p.B * p.Hkv * p.parts * p.NT * p.D;
+  const float* src = p.dkv_part + which * half + (((long long)(b * p.Hkv + hk) * p.parts) * p.NT + s) * p.D + 4 * q4;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int k = 1; k < p.parts; ++k) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(src + (long long)k * p.NT * p.D);
+    acc[0] += x[0];
+    acc[1] += x[1];
+    acc[2] += x[2];
+    acc[3] += x[3];
+  }
+  const float sc = which == 0 ? p.scale : 1.0f;
+  bf16x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[e] * sc);
+  bf16* const dst = (bf16*)(which == 0 ? p.dk : p.dv);
+  *reinterpret_cast<bf16x4*>(dst + (((long long)b * p.S + s) * p.Hkv + hk) * p.D + 4 * q4) = o;
+}
+
 // ---------------------------------------------------------------------------
 // Launch helpers
 
@@ -642,6 +701,15 @@ static hipError_t launch_wide_sched(int sched, const BwdParams& p, int grid, hip
 
 hipError_t launch_bwd_wide(bool causal, const BwdParams& p, int grid, hipStream_t s) {
   return causal ? launch_wide_sched<true>(p.schedule, p, grid, s) : launch_wide_sched<false>(p.schedule, p, grid, s);
+}
+
+hipError_t launch_dkv_finalize(const DkvFinParams& p, hipStream_t s) {
+  const long long total = 2LL * p.B * p.Hkv * p.S * (p.D / 4);
+  const long long blocks = (total + 255) / 256;
+  if (blocks < 1) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dkv_finalize, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize_wide(const FinParams& p, hipStream_t s) {

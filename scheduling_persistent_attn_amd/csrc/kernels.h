@@ -43,8 +43,25 @@ struct BwdParams {
   int B, Hq, Hkv, S, N, G;
   int mask, schedule;
   int total_items, items_per_group;
+  // Query heads of a group split over `parts` items per base item (chain or
+  // symmetric pair): item `local` of a group is part local / base_items (its
+  // heads part*Gp .. part*Gp + Gp - 1) of base item local % base_items.  With
+  // parts > 1 each item writes fp32 partial dK/dV to dkv_part, summed by
+  // bwd_dkv_finalize in ascending part order.
+  int parts, Gp, base_items;
+  float* dkv_part;     // [2][B][Hkv][parts][NT][D] fp32 (dK then dV); parts > 1
+  int NT;              // N * T: rows of the padded sequence
   float scale, scale_log2e;
   long long spin_ticks;
+};
+
+struct DkvFinParams {
+  const float* dkv_part;  // as in BwdParams
+  void* dk;
+  void* dv;
+  const int* ctrl;        // the error flag ctrl[1] up: write nothing
+  int B, Hkv, S, NT, D, parts;
+  float scale;            // dK = scale * sum over the parts
 };
 
 struct FinParams {
@@ -81,6 +98,8 @@ int bwd_block_threads(int T);
 int bwd_wide_blocks_per_cu(bool causal);
 hipError_t launch_bwd_wide(bool causal, const BwdParams& p, int grid, hipStream_t s);
 hipError_t launch_finalize_wide(const FinParams& p, hipStream_t s);
+
+hipError_t launch_dkv_finalize(const DkvFinParams& p, hipStream_t s);
 
 hipError_t launch_preprocess(const PreParams& p, hipStream_t s);
 hipError_t launch_bwd_main(int D, int T, bool causal, const BwdParams& p, int grid,

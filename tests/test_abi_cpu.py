@@ -388,3 +388,43 @@ def test_binding_rejects_mismatched_tensors():
 def test_not_prepared_status():
     assert dash.DASH_ERR_NOT_PREPARED == 8
     assert "not prepared" in dash.dash_status_string(8)
+
+
+def test_head_parts_rule():
+    # with 256-key tiles, the smallest divisor of G giving at least 256 items
+    hp = dash.dash_attn_bwd_head_parts
+    # the 7B-Qwen-shaped causal layer: 4 groups x 32 symmetric pairs = 128
+    # items, so its 7 heads go to 7 parts; its chains (64 per group) suffice
+    assert hp(1, 28, 4, 16384, 128, 1, dash.SYMMETRIC_SHIFT) == 7
+    assert hp(1, 28, 4, 16384, 128, 1, dash.SHIFT) == 1
+    assert hp(1, 28, 4, 16384, 128, 1, dash.AUTO) == 7
+    # the 8B-Llama-shaped layer: 32 groups x 8 pairs = 256 items, no split
+    assert hp(4, 32, 8, 4096, 128, 1, dash.SYMMETRIC_SHIFT) == 1
+    # small shapes take every divisor up to G
+    assert hp(1, 4, 2, 1024, 128, 1, dash.NAIVE) == 2
+    assert hp(1, 6, 1, 1024, 128, 0, dash.SHIFT) == 6
+    # 128-key tiles and single-head groups are never split
+    assert hp(1, 8, 2, 512, 128, 1, dash.NAIVE) == 1
+    assert hp(1, 8, 2, 4096, 64, 1, dash.NAIVE) == 1
+    assert hp(1, 8, 8, 4096, 128, 1, dash.NAIVE) == 1
+    assert hp(1, 3, 2, 4096, 128, 1, dash.NAIVE) == 0  # invalid
+
+
+@pytest.mark.parametrize("s,m", COMBOS)
+@pytest.mark.parametrize("N,G,parts", [(4, 2, 2), (5, 6, 3), (8, 7, 7)])
+def test_library_split_items_equal_oracle(s, m, N, G, parts):
+    # the kernels take item `local` of a group as part local // base of base
+    # item local % base, evaluated by the closed forms with G / parts heads
+    if s == sch.SYMMETRIC_SHIFT and N % 2:
+        return
+    its = sch.items(s, m, N, G, parts)
+    rk = sch.ranks(s, m, N, G)
+    Gp = G // parts
+    base = dash.dash_schedule_num_items(m, s, N)
+    assert len(its) == base * parts
+    for n, it in enumerate(its):
+        k, b = divmod(n, base)
+        assert dash.dash_schedule_item_len(m, s, N, Gp, b) == len(it)
+        for step, (g, i, j) in enumerate(it):
+            gl, il, jl, rl = dash.dash_schedule_task(m, s, N, Gp, b, step)
+            assert (k * Gp + gl, il, jl, rl) == (g, i, j, rk[(g, i, j)]), (n, step)

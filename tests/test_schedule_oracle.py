@@ -326,3 +326,29 @@ def test_planted_diagonal_weight_off_by_one_is_caught(monkeypatch):
     N, c, cd, r = DIAG_CASES[1]
     res = dag.simulate(sch.SHIFT, sch.CAUSAL, N, c=c, c_diag=cd, r=r)
     assert res["makespan"] != cd + (N - 1) * c + N * r
+
+
+def test_golden_n4_g2_split_parts():
+    # a group's heads split over two parts: the hand-written table
+    gold = json.load(open(GOLDEN_G2))
+    N, G = gold["N"], gold["G"]
+    for key, rows in gold["items_parts2"].items():
+        name, mname = key.split("_")
+        s, m = G2_KEYS[name], MASKS[mname]
+        rk = sch.ranks(s, m, N, G)
+        got = [[(g, i, j, rk[(g, i, j)]) for (g, i, j) in it] for it in sch.items(s, m, N, G, parts=2)]
+        assert got == [_parse_item(r) for r in rows], key
+
+
+@pytest.mark.parametrize("s,m,N", list(_combos((2, 4, 5))))
+@pytest.mark.parametrize("G,parts", [(2, 2), (4, 2), (6, 3), (7, 7)])
+def test_split_parts_cover_every_task_once(s, m, N, G, parts):
+    its = sch.items(s, m, N, G, parts)
+    assert len(its) == parts * len(sch.items(s, m, N, G))
+    tasks = [t for it in its for t in it]
+    assert sorted(tasks) == sorted(t for it in sch.items(s, m, N, G) for t in it)
+    # each item serves the heads of one part only, and the parts come in order
+    n_base = len(its) // parts
+    for n, it in enumerate(its):
+        k = n // n_base
+        assert all(k * (G // parts) <= g < (k + 1) * (G // parts) for (g, _, _) in it)
