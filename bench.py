@@ -172,6 +172,14 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
     S, D = x["q"].shape[1], x["q"].shape[3]
     waves = dash.dash_attn_bwd_grid_size(S, D, mask) * dash.dash_attn_tile_size(S, D) // 32
     out["turn_waits"] = wst["waits"]
+    # the shader clock of the last timed launch: workgroup 0's s_memtime and
+    # 100 MHz s_memrealtime stamps at the kernel's start and exit (control
+    # words 8-15 of the workspace)
+    st = ws[32:64].view(torch.int64).cpu().tolist()
+    if st[3] > st[1] and st[2] > st[0]:
+        out["sclk_mhz"] = round(100.0 * (st[2] - st[0]) / (st[3] - st[1]), 1)
+    out["head_parts"] = dash.dash_attn_bwd_head_parts(x["q"].shape[0], x["q"].shape[2], Hkv, S, D,
+                                                      mask, sched)
     out["wait_fraction"] = wst["wait_seconds"] / (waves * kern[-1] * 1e-3)
     if warmup > 0:
         out["repro"] = reproducibility(dash, step, bits, ref, ws)

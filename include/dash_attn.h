@@ -122,7 +122,10 @@ int dash_attn_bwd_head_parts(int B, int Hq, int Hkv, int S, int D, int mask, int
  *   ctrl      64 x int32   [0] work-dispatch counter, [1] error flag
  *                          (watchdog or not prepared), [2] number of waits
  *                          that timed out, [3] always zero, [4] set when a
- *                          run found the workspace not prepared
+ *                          run found the workspace not prepared, [8..15]
+ *                          four uint64: shader-clock and 100 MHz-clock
+ *                          stamps of workgroup 0 at the persistent kernel's
+ *                          start and exit (their ratio is the clock it ran at)
  *   waits     4096 x 4 uint64: per wave of the persistent grid (slot =
  *             workgroup * waves per workgroup + wave), the turn waits that
  *             found the turn not yet taken: [0] count, [1] polls, [2]

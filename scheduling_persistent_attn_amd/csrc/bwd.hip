@@ -529,6 +529,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   int sb = 0;  // dS buffer of the current pass (of three)
   bool acc_tail = false;  // the last four vector memory operations are partial-sum loads
   bool first_item = true;
+  if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 8);
   for (;;) {
     __syncthreads();  // previous item's LDS use complete
     int* const misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
@@ -536,7 +537,10 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
     first_item = false;
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(misc[0]);
-    if (item >= p.total_items) break;
+    if (item >= p.total_items) {
+      if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 12);
+      break;
+    }
     const int grp = item / p.items_per_group;
     const int local = item - grp * p.items_per_group;
     const int b = grp / p.Hkv, hk = grp - b * p.Hkv;

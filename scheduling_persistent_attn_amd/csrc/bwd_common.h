@@ -118,6 +118,17 @@ __device__ __forceinline__ bool wait_turn(const int* cnt, int rank, int* ctrl,
   return ok != 0;
 }
 
+// The shader clock (s_memtime) and the constant 100 MHz clock (s_memrealtime)
+// into four control words; workgroup 0 stamps them when the persistent
+// kernel starts (ctrl[8..11]) and when it leaves (ctrl[12..15]), and the
+// ratio of the two intervals is the clock the compute unit ran at.
+__device__ __forceinline__ void clock_stamp(int* at) {
+  const unsigned long long t = clock64(), r = wall_clock64();
+  unsigned long long* w = reinterpret_cast<unsigned long long*>(at);
+  __hip_atomic_store(w, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(w + 1, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The next item index from the work-dispatch counter ctrl[0] (called by one
 // thread per workgroup).  Each launch on a prepared workspace ends with one
 // draw past the end per workgroup, so its draws are all below total + grid.  A

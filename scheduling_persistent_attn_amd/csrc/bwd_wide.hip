@@ -384,6 +384,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
   int sb = 0;
   bool acc_tail = false;  // the last two vector memory operations are partial-sum loads
   bool first_item = true;
+  if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 8);
   for (;;) {
     __syncthreads();
     int* const misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
@@ -391,7 +392,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
     first_item = false;
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(misc[0]);
-    if (item >= p.total_items) break;
+    if (item >= p.total_items) {
+      if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 12);
+      break;
+    }
     const int grp = item / p.items_per_group;
     const int local = item - grp * p.items_per_group;
     const int b = grp / p.Hkv, hk = grp - b * p.Hkv;
