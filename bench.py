@@ -364,6 +364,79 @@ def sim_report():
                                       "deadlock": bool(res["deadlock"])}), flush=True)
 
 
+def trace_report(dash, name):
+    """Per-task timelines from the debug build's trace beside the simulator.
+
+    Runs every deterministic schedule of a workload once with the traced
+    library and prints one JSON line each: the measured makespan (first task
+    start to last task end), the mean task time, the wave time spent outside
+    tasks (idle or between items) as a share of the grid's time, and the
+    simulator's critical path for the same shape and grid with r/c = 0.1,
+    priced at one task cost for every schedule (the smallest median task time
+    among them: a task that waited for a turn is slower by its wait)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from scheduling_persistent_attn_amd.inputs import make_inputs
+
+    L = dash.trace_lib()
+    cfg = CONFIGS[name]
+    B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    mask = 1 if cfg["causal"] else 0
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    G = Hq // Hkv
+    x = make_inputs(B, S, Hq, Hkv, D, seed=1000, device="cuda")
+    o, lse = dash.forward(x["q"], x["k"], x["v"], cfg["causal"])
+    dq, dk, dv = (torch.empty_like(x[k]) for k in ("q", "k", "v"))
+    P = dash.dash_attn_bwd_grid_size(S, D, mask)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    names = {v: k for k, v in dash.SCHEDULES.items()}
+    rows = []
+    for sched in (dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT, dash.SYMMETRIC_SHIFT):
+        if sched == dash.SYMMETRIC_SHIFT and (not mask or N % 2):
+            continue
+        n = L.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, mask, sched)
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        for _ in range(2):  # the second run is the one read
+            ws.zero_()
+            st = L.dash_attn_bwd(ptr(x["q"]), ptr(x["k"]), ptr(x["v"]), ptr(o), ptr(x["do"]), ptr(lse),
+                                 ptr(dq), ptr(dk), ptr(dv), B, Hq, Hkv, S, D, mask, sched, ptr(ws), n, s)
+            assert st == 0 and L.dash_attn_bwd_check(ptr(ws), s) == 0
+        parts = dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, mask, sched)
+        Gp = G // parts
+        paired = sched == dash.SYMMETRIC_SHIFT
+        tlen = Gp * (N + 1 if paired else N)
+        items = B * Hkv * parts * dash.dash_schedule_num_items(mask, sched, N)
+        nrec = items * tlen
+        region = (nrec * 64 + 255) // 256 * 256
+        start = (n - region) // 8
+        rec = ws.view(torch.int64)[start:start + nrec * 8].cpu().numpy().reshape(nrec, 8)
+        rec = rec[rec[:, 3] != 0]
+        t0, t1 = rec[:, 3].astype(float), rec[:, 4].astype(float)
+        dur = (t1 - t0) / 100.0  # microseconds (100 MHz clock)
+        span = (t1.max() - t0.min()) / 100.0
+        sim = dash.dash_sim_run(mask, sched, N, Gp, B * Hkv * parts, P, 1, 1.0, 1.0, 0.1)
+        rows.append({"workload": name, "schedule": names[sched], "tile": T, "head_parts": parts,
+                     "tasks": int(len(rec)), "grid": P,
+                     "measured_makespan_us": round(span, 1),
+                     "mean_task_us": round(float(dur.mean()), 2),
+                     "median_task_us": round(float(np.median(dur)), 2),
+                     "outside_tasks_fraction": round(1.0 - float(dur.sum()) / (P * span), 4),
+                     "simulated_critical_path_tasks": round(sim["makespan"], 2),
+                     "simulated_efficiency": round(sim["efficiency"], 4)})
+        del ws
+    # one task cost for every schedule: the smallest median task time (tasks
+    # that waited for a turn are in the tail of their schedule's distribution)
+    c = min(r["median_task_us"] for r in rows)
+    for r in rows:
+        r["task_cost_us"] = c
+        r["simulated_makespan_us"] = round(r["simulated_critical_path_tasks"] * c, 1)
+        r["measured_over_simulated"] = round(r["measured_makespan_us"] / r["simulated_makespan_us"], 4)
+        print(json.dumps(r), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,6 +451,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--trace-report", action="store_true",
+                    help="only run the traced debug build once per deterministic schedule of "
+                         "--config and compare the measured task timelines with the simulator")
     ap.add_argument("--sim-report", action="store_true",
                     help="only print the schedule simulator's critical paths for every "
                          "workload and schedule (CPU; no GPU needed)")
@@ -392,6 +468,10 @@ def main():
 
     import torch
     import scheduling_persistent_attn_amd as dash
+
+    if args.trace_report:
+        trace_report(dash, args.config)
+        return
 
     if args.copy_calibration:
         n = 1 << 30

@@ -11,6 +11,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdash_attn.so")
+# the debug build: the same library with a per-task trace in the workspace
+TRACE_LIB_PATH = os.path.join(HERE, "libdash_attn_trace.so")
 
 MASK_FULL, MASK_CAUSAL = 0, 1
 NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT, ATOMIC, AUTO = 0, 1, 2, 3, 4, 5
@@ -58,17 +60,31 @@ class SimResult(ctypes.Structure):
 
 
 _lib = None
+_trace_lib = None
 
 
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libdash_attn.so is not built (run "
-                           "`python -m scheduling_persistent_attn_amd.build`)")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def trace_lib():
+    """The debug build (per-task trace in the workspace); raises if it has not
+    been built.  Same entry points as lib()."""
+    global _trace_lib
+    if _trace_lib is None:
+        _trace_lib = _load(TRACE_LIB_PATH)
+    return _trace_lib
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built (run `python -m scheduling_persistent_attn_amd.build`)"
+                           % os.path.basename(path))
+    L = ctypes.CDLL(path)
     i, p, sz, d = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_double
     L.dash_attn_tile_size.argtypes = [i, i]
     L.dash_attn_tile_size.restype = i
@@ -111,7 +127,6 @@ def lib():
     L.dash_sim_select.restype = i
     L.dash_attn_bwd_auto_schedule.argtypes = [i] * 6
     L.dash_attn_bwd_auto_schedule.restype = i
-    _lib = L
     return L
 
 

@@ -44,32 +44,43 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
+# The debug build with the per-task trace (DASH_TASK_TRACE): the sources that
+# read the flag are compiled again with it and linked into a second library.
+TRACE_LIB = os.path.join(HERE, "libdash_attn_trace.so")
+TRACED = ("bwd.hip", "bwd_wide.hip", "api.cpp")
+
+
 def build(verbose=False):
     cc = hipcc()
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
 
-    def compile_one(src):
-        obj = os.path.join(objdir, src + ".o")
+    def compile_one(job):
+        src, traced = job
+        obj = os.path.join(objdir, src + (".trace.o" if traced else ".o"))
+        flags = ["-DDASH_TASK_TRACE=1"] if traced else []
         if src in HOST_ONLY:
-            cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = ["g++", "-O2", "-std=c++17", "-fPIC"] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
         else:
-            cmd = [cc] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc] + COMMON + EXTRA.get(src, []) + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("compile failed: %s\n%s%s" % (" ".join(cmd), res.stdout, res.stderr))
         return obj
 
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), res.stdout, res.stderr))
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+    jobs = [(src, False) for src in SOURCES] + [(src, True) for src in TRACED]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = dict(zip(jobs, ex.map(compile_one, jobs)))
+    for lib, traced in ((LIB, False), (TRACE_LIB, True)):
+        parts = [objs[(src, traced and src in TRACED)] for src in SOURCES]
+        tmp = lib + ".tmp"
+        cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + parts
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), res.stdout, res.stderr))
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

@@ -69,8 +69,8 @@ int slices_per_tile(int T, int D) { return T == 256 ? T * D / 512 : T * D / 1024
 
 struct Layout {
   int T = 0, N = 0, NW = 0, parts = 1;
-  size_t ctrl = 0, waits = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, dkvp = 0, total = 0;
-  long long n_counters = 0, n_rows = 0, n_dqacc = 0, n_dkvp = 0;
+  size_t ctrl = 0, waits = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, dkvp = 0, trace = 0, total = 0;
+  long long n_counters = 0, n_rows = 0, n_dqacc = 0, n_dkvp = 0, n_trace = 0;
 };
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -111,6 +111,11 @@ int head_parts(int B, int Hkv, int G, int N, int T, int mask, int schedule) {
   return G;
 }
 
+// Trace records per item: its longest task list.
+int trace_len(int mask, int schedule, int N, int Gp) {
+  return Gp * (dash::paired_items(mask, schedule, N) ? N + 1 : N);
+}
+
 int make_layout(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, Layout* L) {
   L->T = dash_attn_tile_size(S, D);
   if (L->T == 0) return DASH_ERR_UNSUPPORTED;
@@ -143,6 +148,21 @@ int make_layout(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, La
   L->dkvp = off;
   L->n_dkvp = L->parts > 1 ? 2LL * B * Hkv * L->parts * L->N * L->T * D : 0;
   off += round256((size_t)L->n_dkvp * sizeof(float));
+#ifdef DASH_TASK_TRACE
+  // the debug build's task trace: 64 bytes per (item, step), for the
+  // longest item of any schedule the call could run
+  L->trace = off;
+  L->n_trace = 0;
+  for (int s = DASH_SCHED_NAIVE; s <= DASH_SCHED_ATOMIC; ++s) {
+    if (schedule != DASH_SCHED_AUTO && s != schedule) continue;
+    if (s == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || L->N % 2 != 0)) continue;
+    const int parts = head_parts(B, Hkv, Hq / Hkv, L->N, L->T, mask, s);
+    const long long items = (long long)B * Hkv * parts * dash::items_per_group(mask, s, L->N);
+    const long long n = items * trace_len(mask, s, L->N, Hq / Hkv / parts);
+    L->n_trace = n > L->n_trace ? n : L->n_trace;
+  }
+  off += round256((size_t)L->n_trace * 64);
+#endif
   L->total = off;
   return DASH_OK;
 }
@@ -424,6 +444,13 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   bp.base_items = base_items;
   bp.dkv_part = L.parts > 1 ? (float*)(ws + L.dkvp) : nullptr;
   bp.NT = L.N * L.T;
+#ifdef DASH_TASK_TRACE
+  bp.trace = (unsigned long long*)(ws + L.trace);
+  bp.trace_len = trace_len(mask, schedule, L.N, bp.Gp);
+#else
+  bp.trace = nullptr;
+  bp.trace_len = 0;
+#endif
   bp.scale = (float)(1.0 / __builtin_sqrt((double)D));
   bp.scale_log2e = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   bp.spin_ticks = g_watchdog_us.load() * dev->wall_khz / 1000;

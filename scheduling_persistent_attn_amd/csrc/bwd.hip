@@ -555,6 +555,9 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
       const int i = t.i, j = t.j, h = hk * G + t.g;
       const bool has_next = step + 1 < len;
       if (has_next) tn = task_at(mask, SCHED, N, G, local, step + 1);
+#ifdef DASH_TASK_TRACE
+      unsigned long long* const trec = trace_begin(p, item, step, t.g, i, j, t.rank);
+#endif
       if (t.seg_begin) {
         // new KV tile: K through LDS into this wave's K and K^T fragments, V
         // rows straight into registers
@@ -751,6 +754,9 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
         sb = sb == 2 ? 0 : sb + 1;
       }
 
+#ifdef DASH_TASK_TRACE
+      trace_end(trec);
+#endif
       if (t.seg_end) {
         // dK = scale * dS^T Q, dV = P^T dO of key/value tile i, bf16
         if (i * T + key_local < S) {

@@ -415,6 +415,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
       const int i = t.i, j = t.j, h = h0 + t.g;
       const bool has_next = step + 1 < len;
       if (has_next) tn = task_at(mask, SCHED, N, Gp, base, step + 1);
+#ifdef DASH_TASK_TRACE
+      unsigned long long* const trec = trace_begin(p, item, step, h - hk * G, i, j, t.rank);
+#endif
       if (t.seg_begin) {
         // new KV tile: K into LDS, V rows of this wave's keys into registers
         __syncthreads();  // the K tile of the previous run is no longer read
@@ -553,6 +556,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
         sb = sb == 2 ? 0 : sb + 1;
       }
 
+#ifdef DASH_TASK_TRACE
+      trace_end(trec);
+#endif
       if (t.seg_end && p.parts > 1) {
         // this part's fp32 dK/dV of key/value tile i (unscaled), summed over
         // the parts by bwd_dkv_finalize; rows past S are written too (the

@@ -53,7 +53,32 @@ struct BwdParams {
   int NT;              // N * T: rows of the padded sequence
   float scale, scale_log2e;
   long long spin_ticks;
+  // Task trace of the debug build (compiled with DASH_TASK_TRACE; NULL
+  // otherwise): record item * trace_len + step, 8 uint64 each -- [0] item |
+  // step << 32, [1] g | i << 16 | j << 32 | rank << 48, [2] workgroup, [3]
+  // and [4] the 100 MHz wall clock when the task starts and ends.
+  unsigned long long* trace;
+  int trace_len;
 };
+
+#ifdef DASH_TASK_TRACE
+// Start of a task's trace record (thread 0 of the workgroup; vector stores).
+__device__ __forceinline__ unsigned long long* trace_begin(const BwdParams& p, int item, int step, int g, int i,
+                                                          int j, int rank) {
+  unsigned long long* r = p.trace + ((long long)item * p.trace_len + step) * 8;
+  if (threadIdx.x == 0) {
+    r[0] = (unsigned)item | ((unsigned long long)(unsigned)step << 32);
+    r[1] = (unsigned long long)(unsigned)g | ((unsigned long long)(unsigned)i << 16) |
+           ((unsigned long long)(unsigned)j << 32) | ((unsigned long long)(unsigned)rank << 48);
+    r[2] = blockIdx.x;
+    r[3] = wall_clock64();
+  }
+  return r;
+}
+__device__ __forceinline__ void trace_end(unsigned long long* r) {
+  if (threadIdx.x == 0) r[4] = wall_clock64();
+}
+#endif
 
 struct DkvFinParams {
   const float* dkv_part;  // as in BwdParams
