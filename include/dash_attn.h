@@ -70,6 +70,10 @@ enum dash_mask { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 };
  *                   and device by the schedule simulator below (see
  *                   dash_attn_bwd_auto_schedule); deterministic like the
  *                   schedule it resolves to.
+ *  TABLE            a deterministic schedule written out task by task (a
+ *                   searched one, see dash_schedule_search); run only by
+ *                   dash_attn_bwd_table.  dash_attn_bwd_workspace_size and
+ *                   dash_attn_bwd_prepare accept it.
  */
 enum dash_schedule {
   DASH_SCHED_NAIVE = 0,
@@ -77,7 +81,8 @@ enum dash_schedule {
   DASH_SCHED_SHIFT = 2,
   DASH_SCHED_SYMMETRIC_SHIFT = 3,
   DASH_SCHED_ATOMIC = 4,
-  DASH_SCHED_AUTO = 5
+  DASH_SCHED_AUTO = 5,
+  DASH_SCHED_TABLE = 6
 };
 
 enum dash_status {
@@ -92,9 +97,17 @@ enum dash_status {
   DASH_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required     */
   DASH_ERR_HIP = 6,           /* a HIP runtime call or launch failed         */
   DASH_ERR_TIMEOUT = 7,       /* the device watchdog fired during a backward */
-  DASH_ERR_NOT_PREPARED = 8   /* dash_attn_bwd_run found a workspace that
+  DASH_ERR_NOT_PREPARED = 8,  /* dash_attn_bwd_run found a workspace that
                                  dash_attn_bwd_prepare had not reset since
                                  the previous run; nothing was computed      */
+  DASH_ERR_TABLE = 9          /* a task table that does not cover every tile
+                                 of every head once, whose ranks are not a
+                                 permutation per dQ tile, that splits a
+                                 key/value tile's tasks, or whose hand-offs
+                                 could wait forever (see
+                                 dash_schedule_table_check); from
+                                 dash_attn_bwd_check: the kernel refused the
+                                 table, nothing was computed                 */
 };
 
 /* Query-tile and key/value-tile edge T used for a problem (both sides use the
@@ -120,9 +133,11 @@ int dash_attn_bwd_head_parts(int B, int Hq, int Hkv, int S, int D, int mask, int
 /* Bytes of workspace dash_attn_bwd needs for these arguments, or 0 if the
  * arguments are invalid.  Layout (offsets rounded up to 256 bytes):
  *   ctrl      64 x int32   [0] work-dispatch counter, [1] error flag
- *                          (watchdog or not prepared), [2] number of waits
- *                          that timed out, [3] always zero, [4] set when a
- *                          run found the workspace not prepared, [8..15]
+ *                          (watchdog, not prepared or table refused), [2]
+ *                          number of waits that timed out, [3] always
+ *                          zero, [4] set when a run found the workspace not
+ *                          prepared, [5] set when the kernel refused a task
+ *                          table (dash_attn_bwd_table), [8..15]
  *                          four uint64: shader-clock and 100 MHz-clock
  *                          stamps of workgroup 0 at the persistent kernel's
  *                          start and exit (their ratio is the clock it ran at)
@@ -232,9 +247,10 @@ int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const voi
                           void* stream);
 
 /* Waits for the stream, then reports DASH_ERR_NOT_PREPARED if the last
- * backward run on this workspace found it not prepared, DASH_ERR_TIMEOUT if
- * its watchdog fired, DASH_ERR_HIP on a runtime error, else DASH_OK.  Reads
- * 16 bytes of the workspace. */
+ * backward run on this workspace found it not prepared, DASH_ERR_TABLE if the
+ * kernel refused its task table, DASH_ERR_TIMEOUT if its watchdog fired,
+ * DASH_ERR_HIP on a runtime error, else DASH_OK.  Reads 20 bytes of the
+ * workspace. */
 int dash_attn_bwd_check(const void* workspace, void* stream);
 
 /* Sums the turn-wait counters the last backward on this workspace left in it
@@ -342,6 +358,112 @@ int dash_sim_run(int mask, int schedule, int N, int G, int groups, int P,
 int dash_sim_select(int mask, int N, int G, int groups, int P, int dispatch,
                     double c_full, double c_diag, double r, int* schedule,
                     dash_sim_result* out);
+
+/* ---------------------------------------------------------------------------
+ * Task tables: a schedule written out task by task (host arrays), searched,
+ * checked, packed for the device and run.  The pages frame scheduling as
+ * minimising the backward DAG's critical path and leave the choice per shape
+ * and hardware open (technical summary, sections 2 and 2.1); the closed forms
+ * above are members of the family searched here.
+ *
+ * A table describes one (batch, key/value head) group; every group runs it.
+ *   items          number of items (1..N): what a workgroup takes at a time
+ *   item_offsets   items + 1 ints: item k is tasks item_offsets[k] ..
+ *                  item_offsets[k+1] - 1, item_offsets[0] = 0, strictly
+ *                  increasing, item_offsets[items] = number of tasks
+ *   tasks          4 ints per task: query head g (0..G-1), key/value tile i,
+ *                  query tile j, rank (position of this contribution in the
+ *                  reduction order of dQ tile (g, j), 0..n_j - 1 where n_j =
+ *                  N for a full mask and j + 1 for a causal one)
+ * Valid when every unmasked (g, i, j) appears exactly once, the ranks of each
+ * dQ tile are a permutation, and all tasks of a key/value tile (every head
+ * and query tile) form one unbroken run inside one item (the unit keeps its
+ * dK/dV in registers, section 2.1).  Tasks run in item order; dispatch gives
+ * items to workgroups in order, group by group.
+ *
+ * Deadlock freedom on P workgroups (dash_schedule_table_check): the waits-for
+ * graph of the kernels' pipelined hand-offs -- within a run the turn of pass
+ * n is taken after pass n+1 and the slice published in pass n+3 (passes per
+ * task: 8 for 256-key tiles, 4 for 128-key tiles at D = 128, 2 otherwise) --
+ * has no cycle, and the items split into consecutive dispatch blocks of at
+ * most P items where no item waits on a later block.
+ */
+
+/* Family kinds of dash_schedule_search (family[0]). */
+enum dash_family {
+  DASH_FAMILY_SYMMETRIC = 0,  /* symmetric pairs (causal, even N)            */
+  DASH_FAMILY_SHIFT = 1,      /* cyclic walk from the diagonal (causal: the
+                                 diagonal upward)                            */
+  DASH_FAMILY_DESCENDING = 2, /* query tiles from the last down              */
+  DASH_FAMILY_ASCENDING = 3   /* query tiles from the first up (full masks)  */
+};
+
+/* Tasks in one group's table: G * N * N (full) or G * N(N+1)/2 (causal);
+ * -1 if invalid. */
+long long dash_schedule_table_tasks(int mask, int N, int G);
+
+/* A closed-form deterministic schedule (NAIVE .. SYMMETRIC_SHIFT) written as
+ * a table; item_offsets needs N + 1 ints, tasks 4 ints per task. */
+int dash_schedule_table_closed_form(int mask, int schedule, int N, int G, int* items,
+                                    int* item_offsets, int* tasks);
+
+/* DASH_OK if the table is valid for tiles of dash_attn_tile_size(S, D) and
+ * deadlock free on P workgroups, DASH_ERR_TABLE if not; DASH_ERR_UNSUPPORTED
+ * for more than 2^24 tasks, or tasks x passes. */
+int dash_schedule_table_check(int S, int D, int mask, int G, int P, int items,
+                              const int* item_offsets, const int* tasks);
+
+/* Checks a table as dash_schedule_table_check does (on any grid wide enough
+ * for its widest dispatch block) and writes its device form to `out` (host
+ * memory; the caller copies it to device memory and passes that to
+ * dash_attn_bwd_table).  Returns the bytes the device form takes (0 when the
+ * table is invalid); with out == NULL only the size.  *status (may be NULL)
+ * gets DASH_OK, the table's error, or DASH_ERR_WORKSPACE when out_bytes is
+ * too small. */
+size_t dash_schedule_table_pack(int S, int D, int mask, int G, int items, const int* item_offsets,
+                                const int* tasks, void* out, size_t out_bytes, int* status);
+
+/* dash_sim_run for a schedule given as a table (N tiles, G heads); the table
+ * must be valid (else DASH_ERR_TABLE). */
+int dash_sim_table(int mask, int N, int G, int groups, int P, int dispatch, double c_full,
+                   double c_diag, double r, int items, const int* item_offsets, const int* tasks,
+                   dash_sim_result* out);
+
+/* Search over a family of block-wise lockstep walks for the shortest
+ * simulated critical path (dynamic dispatch, `groups` groups on P
+ * workgroups, weights as in dash_sim_run).  Candidates, in tie-break order:
+ * each family kind that applies (SYMMETRIC, SHIFT, DESCENDING, ASCENDING),
+ * units (chains, or symmetric pairs) in ascending then descending order, and
+ * dispatch blocks of min(units, P), half that, and 1 consecutive units; dQ
+ * tile (g, j) is reduced in the order (block, step at which the unit reaches
+ * j, unit position).  The closed forms are members (e.g. SHIFT = shift kind,
+ * ascending, one block), so the result is never worse than the best closed
+ * form that runs on P workgroups, and the family reaches N > P, where the
+ * shift family cannot run.  Candidates that fail dash_schedule_table_check
+ * on P are skipped.  Writes the winner (item_offsets: N + 1 ints, tasks: 4
+ * ints per task), family = {kind, order (0 ascending), block} (may be NULL)
+ * and its report (may be NULL). */
+int dash_schedule_search(int S, int D, int mask, int G, int groups, int P, double c_full,
+                         double c_diag, double r, int* items, int* item_offsets, int* tasks,
+                         int* family, dash_sim_result* out);
+
+/* The backward of dash_attn_bwd under a task table.  `table` is the device
+ * copy (table_bytes bytes, 4-byte aligned) of what dash_schedule_table_pack
+ * wrote for this S, D, mask and G = Hq / Hkv, with `items` items; the caller
+ * owns it and must not change it while the call runs.  `grid` caps the
+ * persistent workgroups (0 = dash_attn_bwd_grid_size; else 1 .. that), e.g.
+ * to leave compute units to concurrent work; the launch uses min(grid,
+ * B * Hkv * items).  The host checks sizes; the kernel checks the table's
+ * header (shape, mask, passes, items, tasks) and that the launch is at least
+ * as wide as the table's widest dispatch block; on a mismatch it computes
+ * nothing and dash_attn_bwd_check reports DASH_ERR_TABLE.  Determinism
+ * contract as for dash_attn_bwd: bitwise identical results for a fixed
+ * table.  Workspace: dash_attn_bwd_workspace_size(..., DASH_SCHED_TABLE). */
+int dash_attn_bwd_table(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int S, int D, int mask, const void* table,
+                        size_t table_bytes, int items, int grid, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,14 +32,17 @@ import heapq
 from . import schedule as sch
 
 
-def group_items(schedule, mask, N, G, groups):
+def group_items(schedule, mask, N, G, groups, item_lists=None):
     """All items of all groups, in global dispatch order: list of task lists.
 
-    A task is (group, g, i, j).
+    A task is (group, g, i, j).  item_lists, when given, are one group's items
+    (lists of (g, i, j)) written out directly -- a schedule given as a table --
+    and replace the closed form of `schedule`.
     """
     out = []
+    base = sch.items(schedule, mask, N, G) if item_lists is None else item_lists
     for grp in range(groups):
-        for it in sch.items(schedule, mask, N, G):
+        for it in base:
             out.append([(grp, g, i, j) for (g, i, j) in it])
     return out
 
@@ -48,10 +51,11 @@ def task_cost(mask, i, j, c, c_diag):
     return c_diag if (mask == sch.CAUSAL and i == j) else c
 
 
-def replay(schedule, mask, N, G, groups, P, dispatch, c, c_diag, r, rank_map=None):
+def replay(schedule, mask, N, G, groups, P, dispatch, c, c_diag, r, rank_map=None,
+           item_lists=None):
     """Event-driven replay.  Returns dict with makespan, assignment, times,
     deadlock flag."""
-    its = group_items(schedule, mask, N, G, groups)
+    its = group_items(schedule, mask, N, G, groups, item_lists)
     rk = sch.ranks(schedule, mask, N, G) if rank_map is None else rank_map
     # F time of (group, g, j, rank) once known
     done = {}
@@ -116,10 +120,11 @@ def replay(schedule, mask, N, G, groups, P, dispatch, c, c_diag, r, rank_map=Non
             "deadlock": deadlock}
 
 
-def build_dag(schedule, mask, N, G, groups, P, assign, c, c_diag, r, rank_map=None):
+def build_dag(schedule, mask, N, G, groups, P, assign, c, c_diag, r, rank_map=None,
+              item_lists=None):
     """Explicit event graph.  Returns (nodes, base_edges, order_edges) where an
     edge is (u, v, weight) and a node is (task, kind)."""
-    its = group_items(schedule, mask, N, G, groups)
+    its = group_items(schedule, mask, N, G, groups, item_lists)
     rk = sch.ranks(schedule, mask, N, G) if rank_map is None else rank_map
     nodes = []
     base = []
@@ -176,15 +181,17 @@ def longest_path(nodes, edges):
 
 
 def simulate(schedule, mask, N, G=1, groups=1, P=None, dispatch="static",
-             c=1.0, c_diag=None, r=0.0, rank_map=None):
-    """Replay, DAG, Lemma-1 check.  Returns a dict like the library's report."""
+             c=1.0, c_diag=None, r=0.0, rank_map=None, item_lists=None):
+    """Replay, DAG, Lemma-1 check.  Returns a dict like the library's report.
+    A schedule given as a table passes item_lists and rank_map (schedule is
+    then ignored)."""
     if c_diag is None:
         c_diag = c
-    n_items = len(sch.items(schedule, mask, N, G)) * groups
+    its = group_items(schedule, mask, N, G, groups, item_lists)
+    n_items = len(its)
     if P is None:
         P = n_items
-    rep = replay(schedule, mask, N, G, groups, P, dispatch, c, c_diag, r, rank_map)
-    its = group_items(schedule, mask, N, G, groups)
+    rep = replay(schedule, mask, N, G, groups, P, dispatch, c, c_diag, r, rank_map, item_lists)
     total = sum(task_cost(mask, i, j, c, c_diag) + r
                 for it in its for (_, _, i, j) in it)
     res = {"total_work": total, "deadlock": bool(rep["deadlock"]),
@@ -196,7 +203,7 @@ def simulate(schedule, mask, N, G=1, groups=1, P=None, dispatch="static",
     else:
         assign = rep["assign"]
     nodes, base, order = build_dag(schedule, mask, N, G, groups, P, assign,
-                                   c, c_diag, r, rank_map)
+                                   c, c_diag, r, rank_map, item_lists)
     d_base = longest_path(nodes, base)
     d_full = longest_path(nodes, base + order)
     res["order_edges"] = len(order)

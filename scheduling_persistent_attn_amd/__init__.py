@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libdash_attn.so")
 TRACE_LIB_PATH = os.path.join(HERE, "libdash_attn_trace.so")
 
 MASK_FULL, MASK_CAUSAL = 0, 1
-NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT, ATOMIC, AUTO = 0, 1, 2, 3, 4, 5
+NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT, ATOMIC, AUTO, TABLE = 0, 1, 2, 3, 4, 5, 6
 SCHEDULES = {"naive": NAIVE, "descending_q": DESCENDING_Q, "shift": SHIFT,
              "symmetric_shift": SYMMETRIC_SHIFT, "atomic": ATOMIC}
 DETERMINISTIC = (NAIVE, DESCENDING_Q, SHIFT, SYMMETRIC_SHIFT)
@@ -29,6 +29,10 @@ DASH_ERR_WORKSPACE = 5
 DASH_ERR_HIP = 6
 DASH_ERR_TIMEOUT = 7
 DASH_ERR_NOT_PREPARED = 8
+DASH_ERR_TABLE = 9
+
+# family kinds of dash_schedule_search
+FAMILY_SYMMETRIC, FAMILY_SHIFT, FAMILY_DESCENDING, FAMILY_ASCENDING = 0, 1, 2, 3
 
 SYMBOLS = (
     "dash_attn_tile_size", "dash_attn_bwd_workspace_size", "dash_attn_fwd",
@@ -37,6 +41,8 @@ SYMBOLS = (
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
     "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog", "dash_attn_bwd_wait_stats",
     "dash_attn_bwd_noalloc", "dash_attn_bwd_head_parts",
+    "dash_schedule_table_tasks", "dash_schedule_table_closed_form", "dash_schedule_table_check",
+    "dash_schedule_table_pack", "dash_sim_table", "dash_schedule_search", "dash_attn_bwd_table",
 )
 
 # bytes of the static device workspace behind dash_attn_bwd_noalloc
@@ -127,6 +133,21 @@ def _load(path):
     L.dash_sim_select.restype = i
     L.dash_attn_bwd_auto_schedule.argtypes = [i] * 6
     L.dash_attn_bwd_auto_schedule.restype = i
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.dash_schedule_table_tasks.argtypes = [i, i, i]
+    L.dash_schedule_table_tasks.restype = ctypes.c_longlong
+    L.dash_schedule_table_closed_form.argtypes = [i] * 4 + [ip, ip, ip]
+    L.dash_schedule_table_closed_form.restype = i
+    L.dash_schedule_table_check.argtypes = [i] * 6 + [ip, ip]
+    L.dash_schedule_table_check.restype = i
+    L.dash_schedule_table_pack.argtypes = [i] * 5 + [ip, ip, p, sz, ip]
+    L.dash_schedule_table_pack.restype = sz
+    L.dash_sim_table.argtypes = [i] * 6 + [d, d, d, i, ip, ip, ctypes.POINTER(SimResult)]
+    L.dash_sim_table.restype = i
+    L.dash_schedule_search.argtypes = [i] * 6 + [d, d, d, ip, ip, ip, ip, ctypes.POINTER(SimResult)]
+    L.dash_schedule_search.restype = i
+    L.dash_attn_bwd_table.argtypes = [p] * 9 + [i] * 6 + [p, sz, i, i, p, sz, p]
+    L.dash_attn_bwd_table.restype = i
     return L
 
 
@@ -202,6 +223,110 @@ def dash_sim_run(mask, schedule, N, G=1, groups=1, P=256, dispatch=1,
     if st != DASH_OK:
         raise DashError(st, "dash_sim_run")
     return out.as_dict()
+
+
+# --- task tables ---------------------------------------------------------------
+# A table is (item_offsets, tasks): item_offsets a sequence of items + 1 ints,
+# tasks an [n, 4] array of (g, i, j, rank) rows, as in include/dash_attn.h.
+
+def _int_array(x, shape_tail=()):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    if shape_tail and (a.ndim != 1 + len(shape_tail) or a.shape[1:] != shape_tail):
+        raise ValueError("expected an array of shape [n, %s]" % ", ".join(map(str, shape_tail)))
+    return a
+
+
+def _iptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+
+
+def _table_out(n_tasks, N):
+    import numpy as np
+    return np.zeros(N + 1, dtype=np.int32), np.zeros((n_tasks, 4), dtype=np.int32)
+
+
+def dash_schedule_table_tasks(mask, N, G):
+    return lib().dash_schedule_table_tasks(int(mask), int(N), int(G))
+
+
+def dash_schedule_table_closed_form(mask, schedule, N, G):
+    """A closed-form schedule as a table: (item_offsets, tasks)."""
+    n = dash_schedule_table_tasks(mask, N, G)
+    if n < 0:
+        raise ValueError("invalid mask, N or G")
+    offs, tasks = _table_out(n, N)
+    items = ctypes.c_int()
+    st = lib().dash_schedule_table_closed_form(int(mask), int(schedule), int(N), int(G),
+                                               ctypes.byref(items), _iptr(offs), _iptr(tasks))
+    if st != DASH_OK:
+        raise DashError(st, "dash_schedule_table_closed_form")
+    return offs[:items.value + 1], tasks
+
+
+def dash_schedule_table_check(S, D, mask, G, P, item_offsets, tasks):
+    """Status of the table's checks (DASH_OK or an error code)."""
+    offs = _int_array(item_offsets)
+    tk = _int_array(tasks, (4,))
+    return lib().dash_schedule_table_check(int(S), int(D), int(mask), int(G), int(P),
+                                           len(offs) - 1, _iptr(offs), _iptr(tk))
+
+
+def dash_schedule_table_pack(S, D, mask, G, item_offsets, tasks):
+    """The table's device form as bytes (raises DashError if invalid)."""
+    offs = _int_array(item_offsets)
+    tk = _int_array(tasks, (4,))
+    st = ctypes.c_int()
+    n = lib().dash_schedule_table_pack(int(S), int(D), int(mask), int(G), len(offs) - 1,
+                                       _iptr(offs), _iptr(tk), None, 0, ctypes.byref(st))
+    if st.value != DASH_OK:
+        raise DashError(st.value, "dash_schedule_table_pack")
+    buf = ctypes.create_string_buffer(n)
+    lib().dash_schedule_table_pack(int(S), int(D), int(mask), int(G), len(offs) - 1,
+                                   _iptr(offs), _iptr(tk), buf, n, ctypes.byref(st))
+    if st.value != DASH_OK:
+        raise DashError(st.value, "dash_schedule_table_pack")
+    return buf.raw
+
+
+def dash_sim_table(mask, N, G, groups, P, dispatch, item_offsets, tasks, c_full=1.0,
+                   c_diag=None, r=0.0):
+    if c_diag is None:
+        c_diag = c_full
+    offs = _int_array(item_offsets)
+    tk = _int_array(tasks, (4,))
+    out = SimResult()
+    st = lib().dash_sim_table(int(mask), int(N), int(G), int(groups), int(P), int(dispatch),
+                              float(c_full), float(c_diag), float(r), len(offs) - 1,
+                              _iptr(offs), _iptr(tk), ctypes.byref(out))
+    if st != DASH_OK:
+        raise DashError(st, "dash_sim_table")
+    return out.as_dict()
+
+
+def dash_schedule_search(S, D, mask, G=1, groups=1, P=256, c_full=1.0, c_diag=None, r=0.0):
+    """The searched schedule: dict with item_offsets, tasks, family (kind,
+    order, block) and the simulator's report."""
+    if c_diag is None:
+        c_diag = c_full
+    T = dash_attn_tile_size(S, D)
+    if T == 0 or S < 1:
+        raise ValueError("unsupported S or D")
+    N = (S + T - 1) // T
+    n = dash_schedule_table_tasks(mask, N, G)
+    if n < 0:
+        raise ValueError("invalid mask or G")
+    offs, tasks = _table_out(n, N)
+    items = ctypes.c_int()
+    fam = (ctypes.c_int * 3)()
+    out = SimResult()
+    st = lib().dash_schedule_search(int(S), int(D), int(mask), int(G), int(groups), int(P),
+                                    float(c_full), float(c_diag), float(r), ctypes.byref(items),
+                                    _iptr(offs), _iptr(tasks), fam, ctypes.byref(out))
+    if st != DASH_OK:
+        raise DashError(st, "dash_schedule_search")
+    return {"item_offsets": offs[:items.value + 1], "tasks": tasks,
+            "family": tuple(fam), "report": out.as_dict()}
 
 
 def _stream(stream):
@@ -361,6 +486,33 @@ def dash_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, mask, schedule, str
         raise DashError(st, "dash_attn_bwd_noalloc")
 
 
+def dash_attn_bwd_table(q, k, v, o, dout, lse, dq, dk, dv, mask, table, items, grid, workspace,
+                        stream=None):
+    """dash_attn_bwd under a task table; `table` is a uint8 device tensor
+    holding what dash_schedule_table_pack returned, `items` its item count,
+    `grid` the cap on persistent workgroups (0 = the device's grid)."""
+    import torch
+    _check_tensors([("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)], torch.bfloat16)
+    _check_tensors([("lse", lse)], torch.float32)
+    _check_tensors([("table", table)], torch.uint8)
+    dims = _dims(q, k)
+    dev = _check_layout(dims, [("q", q), ("o", o), ("dout", dout), ("dq", dq)],
+                        [("k", k), ("v", v), ("dk", dk), ("dv", dv)], [("lse", lse)])
+    _check_workspace(workspace, dev)
+    if table is not None and table.device != dev:
+        raise ValueError("table must be on the tensors' device")
+    B, S, Hq, Hkv, D = dims
+    st = lib().dash_attn_bwd_table(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(mask),
+                                   _ptr(table), table.numel() if table is not None else 0,
+                                   int(items), int(grid), _ptr(workspace),
+                                   workspace.numel() if workspace is not None else 0,
+                                   _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd_table")
+
+
 def dash_attn_bwd_check(workspace, stream=None):
     st = lib().dash_attn_bwd_check(_ptr(workspace), _stream(stream))
     if st != DASH_OK:
@@ -405,6 +557,34 @@ def forward(q, k, v, causal):
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     dash_attn_fwd(q, k, v, o, lse, MASK_CAUSAL if causal else MASK_FULL)
     return o, lse
+
+
+def upload_table(q, k, causal, item_offsets, tasks):
+    """Packs a table for q/k's shape and copies it to q's device: (uint8
+    tensor, items)."""
+    import torch
+    B, S, Hq, Hkv, D = _dims(q, k)
+    raw = dash_schedule_table_pack(S, D, MASK_CAUSAL if causal else MASK_FULL, Hq // Hkv,
+                                   item_offsets, tasks)
+    host = torch.frombuffer(bytearray(raw), dtype=torch.uint8)
+    return host.to(q.device), len(item_offsets) - 1
+
+
+def backward_table(q, k, v, o, dout, lse, causal, table, items, grid=0, workspace=None,
+                   stream=None, check=True):
+    """Allocates dq, dk, dv and runs dash_attn_bwd_table (see backward)."""
+    import torch
+    mask = MASK_CAUSAL if causal else MASK_FULL
+    if workspace is None:
+        workspace = new_workspace(q, k, mask, TABLE)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dash_attn_bwd_table(q, k, v, o, dout, lse, dq, dk, dv, mask, table, items, grid,
+                        workspace, stream)
+    if check and q.numel() > 0:
+        dash_attn_bwd_check(workspace, stream)
+    return dq, dk, dv
 
 
 def backward(q, k, v, o, dout, lse, causal, schedule=SHIFT, workspace=None, stream=None,

@@ -15,8 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdash_attn.so")
-SOURCES = ["bwd.hip", "bwd_wide.hip", "fwd.hip", "api.cpp", "sim.cpp"]
-HOST_ONLY = {"sim.cpp"}  # plain C++, no HIP
+SOURCES = ["bwd.hip", "bwd_wide.hip", "fwd.hip", "api.cpp", "sim.cpp", "table.cpp"]
+HOST_ONLY = {"sim.cpp", "table.cpp"}  # plain C++, no HIP
 ARCH = "gfx950"
 
 COMMON = [

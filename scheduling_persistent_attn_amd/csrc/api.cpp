@@ -81,7 +81,8 @@ int check_shape(int B, int Hq, int Hkv, int S, int D, int mask, int schedule) {
   if (Hq % Hkv != 0) return DASH_ERR_SHAPE;
   if (D != 64 && D != 128) return DASH_ERR_UNSUPPORTED;
   if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return DASH_ERR_SCHEDULE_MASK;
-  if (schedule < DASH_SCHED_NAIVE || schedule > DASH_SCHED_AUTO) return DASH_ERR_SCHEDULE_MASK;
+  if ((schedule < DASH_SCHED_NAIVE || schedule > DASH_SCHED_AUTO) && schedule != DASH_SCHED_TABLE)
+    return DASH_ERR_SCHEDULE_MASK;
   return DASH_OK;
 }
 
@@ -95,7 +96,8 @@ constexpr int kSplitTargetItems = 256;
 // largest over the schedules it can resolve to (the workspace then covers
 // any of them).
 int head_parts(int B, int Hkv, int G, int N, int T, int mask, int schedule) {
-  if (T != 256 || G == 1 || N == 0) return 1;
+  // a table keeps every key/value tile's heads in one run
+  if (T != 256 || G == 1 || N == 0 || schedule == DASH_SCHED_TABLE) return 1;
   if (schedule == DASH_SCHED_AUTO) {
     int m = 1;
     for (int s = DASH_SCHED_NAIVE; s <= DASH_SCHED_SYMMETRIC_SHIFT; ++s) {
@@ -161,6 +163,8 @@ int make_layout(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, La
     const long long n = items * trace_len(mask, s, L->N, Hq / Hkv / parts);
     L->n_trace = n > L->n_trace ? n : L->n_trace;
   }
+  // a table schedule: one record per task
+  if (schedule == DASH_SCHED_TABLE) L->n_trace = (long long)B * Hq * L->N * L->N;
   off += round256((size_t)L->n_trace * 64);
 #endif
   L->total = off;
@@ -292,6 +296,7 @@ const char* dash_status_string(int status) {
     case DASH_ERR_HIP: return "HIP runtime error";
     case DASH_ERR_TIMEOUT: return "device watchdog fired in an ordered reduction";
     case DASH_ERR_NOT_PREPARED: return "backward run on a workspace not prepared since the last run";
+    case DASH_ERR_TABLE: return "task table invalid, could deadlock, or refused by the kernel";
     default: return "unknown status";
   }
 }
@@ -336,6 +341,13 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
 
 namespace {
 
+// A table schedule's launch arguments (already checked by the caller).
+struct TableArgs {
+  const void* table;
+  int items;
+  int grid;  // workgroups to launch at most; 0 = the device's persistent grid
+};
+
 // Everything a backward launch needs, checked once.
 struct BwdPlan {
   Layout L;
@@ -353,7 +365,7 @@ struct BwdPlan {
 int plan_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
              int D, int mask, int schedule, void* workspace, size_t workspace_bytes, int need,
-             BwdPlan* P, bool* empty) {
+             BwdPlan* P, bool* empty, const TableArgs* tab = nullptr) {
   *empty = false;
   int st = check_shape(B, Hq, Hkv, S, D, mask, schedule);
   if (st != DASH_OK) return st;
@@ -362,6 +374,8 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (st != DASH_OK) return st;
   if (schedule == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || (L.N % 2) != 0))
     return DASH_ERR_SCHEDULE_MASK;
+  // the main phase of a table schedule needs its table
+  if (schedule == DASH_SCHED_TABLE && (need & 2) && !tab) return DASH_ERR_SCHEDULE_MASK;
   if (B == 0 || S == 0) {
     *empty = true;
     return DASH_OK;
@@ -385,11 +399,12 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   DeviceInfo* dev = nullptr;
   st = device_info(&dev);
   if (st != DASH_OK) return st;
-  const int grid = dev->cus * blocks_per_cu(*dev, D, L.T, mask);
+  int grid = dev->cus * blocks_per_cu(*dev, D, L.T, mask);
   if (grid <= 0) return DASH_ERR_HIP;
   const int G = Hq / Hkv;
-  const int base_items = dash::items_per_group(mask, schedule, L.N);
+  const int base_items = tab ? tab->items : dash::items_per_group(mask, schedule, L.N);
   const int ipg = base_items * L.parts;
+  if (tab && tab->grid > 0) grid = tab->grid;
   // The shift family waits on chains that come later in the dispatch order,
   // so the items of one part of a group must be able to run at once.
   if ((schedule == DASH_SCHED_SHIFT || schedule == DASH_SCHED_SYMMETRIC_SHIFT) && base_items > grid)
@@ -444,6 +459,8 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   bp.base_items = base_items;
   bp.dkv_part = L.parts > 1 ? (float*)(ws + L.dkvp) : nullptr;
   bp.NT = L.N * L.T;
+  bp.table = tab ? (const unsigned*)tab->table : nullptr;
+  bp.table_tasks = tab ? (int)dash_schedule_table_tasks(mask, L.N, G) : 0;
 #ifdef DASH_TASK_TRACE
   bp.trace = (unsigned long long*)(ws + L.trace);
   bp.trace_len = trace_len(mask, schedule, L.N, bp.Gp);
@@ -538,6 +555,39 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v, const void* d
   return launch_main_phase(P, D, mask, (hipStream_t)stream);
 }
 
+int dash_attn_bwd_table(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int Hq, int Hkv, int S, int D, int mask, const void* table,
+                        size_t table_bytes, int items, int grid, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_TABLE);
+  if (st != DASH_OK) return st;
+  if (B == 0 || S == 0) return DASH_OK;  // nothing to launch, as dash_attn_bwd
+  if (!table) return DASH_ERR_NULL;
+  if (!aligned(table, 4)) return DASH_ERR_SHAPE;
+  const int T = dash_attn_tile_size(S, D);
+  const int N = (S + T - 1) / T;
+  const long long n = dash_schedule_table_tasks(mask, N, Hq / Hkv);
+  if (items < 1 || items > N || n < 0) return DASH_ERR_TABLE;
+  if (table_bytes < ((size_t)dash::table_task_words(items) + 2 * (size_t)n) * sizeof(unsigned))
+    return DASH_ERR_TABLE;
+  DeviceInfo* dev = nullptr;
+  st = device_info(&dev);
+  if (st != DASH_OK) return st;
+  const int full = dev->cus * blocks_per_cu(*dev, D, T, mask);
+  if (full <= 0) return DASH_ERR_HIP;
+  if (grid < 0 || grid > full) return DASH_ERR_SHAPE;
+  const TableArgs tab = {table, items, grid};
+  BwdPlan P;
+  bool empty = false;
+  st = plan_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, DASH_SCHED_TABLE,
+                workspace, workspace_bytes, 3, &P, &empty, &tab);
+  if (st != DASH_OK || empty) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
+  return launch_main_phase(P, D, mask, s);
+}
+
 int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
                           int B, int Hq, int Hkv, int S, int D, int mask, int schedule,
@@ -563,12 +613,14 @@ int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const voi
 int dash_attn_bwd_check(const void* workspace, void* stream) {
   if (!workspace) return DASH_ERR_NULL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
-  // ctrl[1] error flag, [2] timed-out waits, [3] always zero, [4] not-prepared mark
-  int flag[4] = {0, 0, 0, 0};
+  // ctrl[1] error flag, [2] timed-out waits, [3] always zero, [4] not-prepared
+  // mark, [5] table-refused mark
+  int flag[5] = {0, 0, 0, 0, 0};
   if (hipMemcpy(flag, (const int*)workspace + 1, sizeof(flag), hipMemcpyDeviceToHost) !=
       hipSuccess)
     return DASH_ERR_HIP;
   if (flag[3]) return DASH_ERR_NOT_PREPARED;
+  if (flag[4]) return DASH_ERR_TABLE;
   return flag[0] ? DASH_ERR_TIMEOUT : DASH_OK;
 }
 

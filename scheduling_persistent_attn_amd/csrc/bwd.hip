@@ -529,6 +529,12 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   int sb = 0;  // dS buffer of the current pass (of three)
   bool acc_tail = false;  // the last four vector memory operations are partial-sum loads
   bool first_item = true;
+  if constexpr (SCHED == SCHED_TABLE) {
+    if (!table_fits(p, NP)) {
+      table_refused(p.ctrl);
+      return;
+    }
+  }
   if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 8);
   for (;;) {
     __syncthreads();  // previous item's LDS use complete
@@ -544,8 +550,9 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
     const int grp = item / p.items_per_group;
     const int local = item - grp * p.items_per_group;
     const int b = grp / p.Hkv, hk = grp - b * p.Hkv;
-    const int len = item_len(mask, SCHED, N, G, local);
-    Task tn = task_at(mask, SCHED, N, G, local, 0);
+    const int first_task = item_first_task<SCHED>(p, local);
+    const int len = item_tasks<SCHED>(p, mask, N, G, local);
+    Task tn = item_task<SCHED>(p, mask, N, G, local, first_task, 0);
     stage_load<D, BQ, C::NW>(stage, p, T, b, hk * G + tn.g, tn.j, 0, true, voffQ, w, lane);
     stage_store<D, BQ, C::NW>(stage, smem + C::OFF_Q + (gp & 1) * C::Q_TILE, smem + C::OFF_DO + (gp & 1) * C::Q_TILE,
                               smem + C::OFF_LD + (gp & 1) * 2 * 4 * BQ, w, lane);
@@ -554,9 +561,11 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
       const Task t = tn;
       const int i = t.i, j = t.j, h = hk * G + t.g;
       const bool has_next = step + 1 < len;
-      if (has_next) tn = task_at(mask, SCHED, N, G, local, step + 1);
+      if (has_next) tn = item_task<SCHED>(p, mask, N, G, local, first_task, step + 1);
 #ifdef DASH_TASK_TRACE
-      unsigned long long* const trec = trace_begin(p, item, step, t.g, i, j, t.rank);
+      const long long rec = SCHED == SCHED_TABLE ? (long long)grp * p.table_tasks + first_task + step
+                                                 : (long long)item * p.trace_len + step;
+      unsigned long long* const trec = trace_begin(p, rec, item, step, t.g, i, j, t.rank);
 #endif
       if (t.seg_begin) {
         // new KV tile: K through LDS into this wave's K and K^T fragments, V
@@ -900,6 +909,9 @@ static hipError_t launch_sched(int sched, const BwdParams& p, int grid, hipStrea
       return hipErrorInvalidValue;
     case SCHED_ATOMIC:
       hipLaunchKernelGGL((bwd_main<D, T, CAUSAL, SCHED_ATOMIC>), dim3(grid), dim3(2 * T), 0, s, p);
+      break;
+    case SCHED_TABLE:
+      hipLaunchKernelGGL((bwd_main<D, T, CAUSAL, SCHED_TABLE>), dim3(grid), dim3(2 * T), 0, s, p);
       break;
     default:
       return hipErrorInvalidValue;

@@ -9,6 +9,7 @@
 
 #include "kernels.h"
 #include "lds_layout.h"
+#include "schedule.h"
 
 namespace dash {
 
@@ -155,6 +156,49 @@ __device__ __forceinline__ int next_item(int* ctrl, int total, bool first) {
 // super-row) and chunk chunk0, because the swizzle repeats every 16 (256-byte
 // rows) or 8 (128-byte rows) super-rows; so one lane offset and a scalar
 // per-block offset address every block.
+// Whether a table schedule's header matches the launch: the shape, mask and
+// passes per task it was checked for, its item and task counts, and a grid
+// at least as wide as its widest dispatch block (the words are uniform).
+__device__ __forceinline__ bool table_fits(const BwdParams& p, int passes) {
+  const unsigned* h = p.table;
+  return h[0] == kTableMagic && h[1] == (unsigned)p.N && h[2] == (unsigned)p.G && h[3] == (unsigned)p.mask &&
+         h[4] == (unsigned)passes && h[5] == (unsigned)p.items_per_group && h[6] <= gridDim.x &&
+         h[7] == (unsigned)p.table_tasks;
+}
+
+// A refused table: every workgroup leaves before touching any buffer, and
+// workgroup 0 raises the error flag and the table mark (vector stores).
+__device__ __forceinline__ void table_refused(int* ctrl) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    __hip_atomic_store(ctrl + 5, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ctrl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Index of an item's first task in its group's task list (tables only) and
+// its task count.
+template <int SCHED>
+__device__ __forceinline__ int item_first_task(const BwdParams& p, int item) {
+  if constexpr (SCHED == SCHED_TABLE) return (int)p.table[kTableHeaderWords + item];
+  return 0;
+}
+template <int SCHED>
+__device__ __forceinline__ int item_tasks(const BwdParams& p, int mask, int N, int G, int item) {
+  if constexpr (SCHED == SCHED_TABLE)
+    return (int)(p.table[kTableHeaderWords + item + 1] - p.table[kTableHeaderWords + item]);
+  return item_len(mask, SCHED, N, G, item);
+}
+// Task `step` of an item (first_task from item_first_task).
+template <int SCHED>
+__device__ __forceinline__ Task item_task(const BwdParams& p, int mask, int N, int G, int item, int first_task,
+                                          int step) {
+  if constexpr (SCHED == SCHED_TABLE) {
+    const unsigned* w = p.table + table_task_words(p.items_per_group) + 2 * (first_task + step);
+    return table_task(w[0], w[1]);
+  }
+  return task_at(mask, SCHED, N, G, item, step);
+}
+
 template <int D, int ROWS, int NW>
 __device__ __forceinline__ void load_tile_async(const bf16* g, int rs, int nvalid, const char* dst,
                                                 int w, int row0, int chunk0) {

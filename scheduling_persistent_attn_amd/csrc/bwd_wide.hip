@@ -384,6 +384,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
   int sb = 0;
   bool acc_tail = false;  // the last two vector memory operations are partial-sum loads
   bool first_item = true;
+  if constexpr (SCHED == SCHED_TABLE) {
+    if (!table_fits(p, NP)) {
+      table_refused(p.ctrl);
+      return;
+    }
+  }
   if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 8);
   for (;;) {
     __syncthreads();
@@ -404,8 +410,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
     const int base = local - part * p.base_items;
     const int Gp = p.Gp;
     const int h0 = hk * G + part * Gp;  // first query head of the part
-    const int len = item_len(mask, SCHED, N, Gp, base);
-    Task tn = task_at(mask, SCHED, N, Gp, base, 0);
+    const int first_task = item_first_task<SCHED>(p, base);
+    const int len = item_tasks<SCHED>(p, mask, N, Gp, base);
+    Task tn = item_task<SCHED>(p, mask, N, Gp, base, first_task, 0);
     stage_load<D, BQ, C::NW>(stage, p, T, b, h0 + tn.g, tn.j, 0, true, voffQ, w, lane);
     stage_store<D, BQ, C::NW>(stage, smem + C::OFF_Q + (gp & 1) * C::Q_TILE, smem + C::OFF_DO + (gp & 1) * C::Q_TILE,
                               smem + C::OFF_LD + (gp & 1) * 2 * 4 * BQ, w, lane);
@@ -414,9 +421,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
       const Task t = tn;
       const int i = t.i, j = t.j, h = h0 + t.g;
       const bool has_next = step + 1 < len;
-      if (has_next) tn = task_at(mask, SCHED, N, Gp, base, step + 1);
+      if (has_next) tn = item_task<SCHED>(p, mask, N, Gp, base, first_task, step + 1);
 #ifdef DASH_TASK_TRACE
-      unsigned long long* const trec = trace_begin(p, item, step, h - hk * G, i, j, t.rank);
+      const long long rec = SCHED == SCHED_TABLE ? (long long)grp * p.table_tasks + first_task + step
+                                                 : (long long)item * p.trace_len + step;
+      unsigned long long* const trec = trace_begin(p, rec, item, step, h - hk * G, i, j, t.rank);
 #endif
       if (t.seg_begin) {
         // new KV tile: K into LDS, V rows of this wave's keys into registers
@@ -702,6 +711,9 @@ static hipError_t launch_wide_sched(int sched, const BwdParams& p, int grid, hip
       return hipErrorInvalidValue;
     case SCHED_ATOMIC:
       hipLaunchKernelGGL((bwd_main_wide<CAUSAL, SCHED_ATOMIC>), dim3(grid), dim3(512), 0, s, p);
+      break;
+    case SCHED_TABLE:
+      hipLaunchKernelGGL((bwd_main_wide<CAUSAL, SCHED_TABLE>), dim3(grid), dim3(512), 0, s, p);
       break;
     default:
       return hipErrorInvalidValue;

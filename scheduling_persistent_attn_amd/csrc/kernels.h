@@ -51,10 +51,15 @@ struct BwdParams {
   int parts, Gp, base_items;
   float* dkv_part;     // [2][B][Hkv][parts][NT][D] fp32 (dK then dV); parts > 1
   int NT;              // N * T: rows of the padded sequence
+  // Table schedules: the packed task table (layout in schedule.h; caller's
+  // device memory) and its tasks per group.  NULL / 0 otherwise.
+  const unsigned* table;
+  int table_tasks;
   float scale, scale_log2e;
   long long spin_ticks;
   // Task trace of the debug build (compiled with DASH_TASK_TRACE; NULL
-  // otherwise): record item * trace_len + step, 8 uint64 each -- [0] item |
+  // otherwise): record item * trace_len + step (for a table schedule, the
+  // task's index group * table_tasks + its table index), 8 uint64 each -- [0] item |
   // step << 32, [1] g | i << 16 | j << 32 | rank << 48, [2] workgroup, [3]
   // and [4] the 100 MHz wall clock when the task starts and ends.
   unsigned long long* trace;
@@ -63,9 +68,9 @@ struct BwdParams {
 
 #ifdef DASH_TASK_TRACE
 // Start of a task's trace record (thread 0 of the workgroup; vector stores).
-__device__ __forceinline__ unsigned long long* trace_begin(const BwdParams& p, int item, int step, int g, int i,
-                                                          int j, int rank) {
-  unsigned long long* r = p.trace + ((long long)item * p.trace_len + step) * 8;
+__device__ __forceinline__ unsigned long long* trace_begin(const BwdParams& p, long long rec, int item, int step,
+                                                          int g, int i, int j, int rank) {
+  unsigned long long* r = p.trace + rec * 8;
   if (threadIdx.x == 0) {
     r[0] = (unsigned)item | ((unsigned long long)(unsigned)step << 32);
     r[1] = (unsigned long long)(unsigned)g | ((unsigned long long)(unsigned)i << 16) |

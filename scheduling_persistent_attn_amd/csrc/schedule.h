@@ -40,7 +40,8 @@
 namespace dash {
 
 enum { MASK_FULL = 0, MASK_CAUSAL = 1 };
-enum { SCHED_NAIVE = 0, SCHED_DESC = 1, SCHED_SHIFT = 2, SCHED_SYM = 3, SCHED_ATOMIC = 4 };
+// SCHED_TABLE: a schedule written out as a task table (see below).
+enum { SCHED_NAIVE = 0, SCHED_DESC = 1, SCHED_SHIFT = 2, SCHED_SYM = 3, SCHED_ATOMIC = 4, SCHED_TABLE = 6 };
 
 struct Task {
   int g, i, j, rank;
@@ -127,6 +128,32 @@ DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
       t.rank = i;
       break;
   }
+  return t;
+}
+
+// Packed device form of a task table (one group's items; every group runs
+// the same table).  Words: a header of kTableHeaderWords -- magic, N, G,
+// mask, passes per task, items, widest dispatch block, tasks -- then the
+// item offsets (items + 1 words, padded to an even count), then two words per
+// task: i | j << 16 and g | rank << 16 | run start << 30 | run end << 31,
+// where a run is a key/value tile's unbroken stretch of tasks in its item.
+// The kernels compare the header with their launch and refuse a table made
+// for another shape or kernel, or a launch with fewer workgroups than the
+// table's widest dispatch block.
+constexpr int kTableHeaderWords = 8;
+constexpr unsigned kTableMagic = 0x54485344u;  // "DSHT"
+
+// Word index of the first task, after the header and the item offsets.
+DASH_HD int table_task_words(int items) { return kTableHeaderWords + ((items + 2) & ~1); }
+
+DASH_HD Task table_task(unsigned w0, unsigned w1) {
+  Task t;
+  t.i = (int)(w0 & 0xffffu);
+  t.j = (int)(w0 >> 16);
+  t.g = (int)(w1 & 0xffffu);
+  t.rank = (int)((w1 >> 16) & 0x3fffu);
+  t.seg_begin = (int)((w1 >> 30) & 1u);
+  t.seg_end = (int)(w1 >> 31);
   return t;
 }
 

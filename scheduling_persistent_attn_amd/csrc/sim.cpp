@@ -21,6 +21,7 @@
 
 #include "../../include/dash_attn.h"
 #include "schedule.h"
+#include "table.h"
 
 namespace {
 
@@ -41,16 +42,17 @@ struct Problem {
   }
 };
 
-bool build(Problem& pb) {
-  const int ipg = dash::items_per_group(pb.mask, pb.schedule, pb.N);
+bool build(Problem& pb, const dash::GroupTable& tb) {
+  const int ipg = (int)tb.offs.size() - 1;
   const int items = ipg * pb.groups;
+  const int per = (int)tb.tasks.size();
   pb.item_first.assign(items + 1, 0);
+  pb.tasks.reserve((size_t)per * pb.groups);
   for (int grp = 0; grp < pb.groups; ++grp) {
     for (int it = 0; it < ipg; ++it) {
       pb.item_first[grp * ipg + it] = (int)pb.tasks.size();
-      const int len = dash::item_len(pb.mask, pb.schedule, pb.N, pb.G, it);
-      for (int s = 0; s < len; ++s) {
-        const dash::Task t = dash::task_at(pb.mask, pb.schedule, pb.N, pb.G, it, s);
+      for (int s = tb.offs[it]; s < tb.offs[it + 1]; ++s) {
+        const dash::TableTask& t = tb.tasks[s];
         pb.tasks.push_back({grp, t.g, t.i, t.j, t.rank, grp * ipg + it});
       }
     }
@@ -223,28 +225,12 @@ bool longest(const Problem& pb, const std::vector<int>& assign, bool with_order,
 
 }  // namespace
 
-extern "C" int dash_sim_run(int mask, int schedule, int N, int G, int groups, int P,
-                            int dispatch, double c_full, double c_diag, double r,
-                            dash_sim_result* out) {
-  if (!out) return DASH_ERR_NULL;
-  if (N < 1 || G < 1 || groups < 1 || P < 1 || (dispatch != 0 && dispatch != 1))
-    return DASH_ERR_SHAPE;
-  if (dash_schedule_num_items(mask, schedule, N) < 0) return DASH_ERR_SCHEDULE_MASK;
-  if (!(c_full >= 0.0) || !(c_diag >= 0.0) || !(r >= 0.0)) return DASH_ERR_SHAPE;
-  const double tasks_est = (double)groups * G * N * (double)N;
-  if (tasks_est > 2.0e7) return DASH_ERR_UNSUPPORTED;
-  Problem pb;
-  pb.mask = mask;
-  pb.schedule = schedule;
-  pb.N = N;
-  pb.G = G;
-  pb.groups = groups;
-  pb.P = P;
-  pb.c = c_full;
-  pb.c_diag = c_diag;
-  pb.r = r;
-  if (!build(pb)) return DASH_ERR_SCHEDULE_MASK;
+namespace {
 
+// Simulation of any schedule given as a table (closed forms included).
+int run_problem(Problem& pb, const dash::GroupTable& tb, int dispatch, dash_sim_result* out) {
+  if (!build(pb, tb)) return DASH_ERR_TABLE;
+  const int P = pb.P;
   std::vector<int> assign;
   double replay_mk = 0.0;
   const bool ok = replay(pb, dispatch, assign, &replay_mk);
@@ -289,6 +275,33 @@ extern "C" int dash_sim_run(int mask, int schedule, int N, int G, int groups, in
   return DASH_OK;
 }
 
+
+}  // namespace
+
+extern "C" int dash_sim_run(int mask, int schedule, int N, int G, int groups, int P,
+                            int dispatch, double c_full, double c_diag, double r,
+                            dash_sim_result* out) {
+  if (!out) return DASH_ERR_NULL;
+  if (N < 1 || G < 1 || groups < 1 || P < 1 || (dispatch != 0 && dispatch != 1))
+    return DASH_ERR_SHAPE;
+  if (dash_schedule_num_items(mask, schedule, N) < 0) return DASH_ERR_SCHEDULE_MASK;
+  if (!(c_full >= 0.0) || !(c_diag >= 0.0) || !(r >= 0.0)) return DASH_ERR_SHAPE;
+  const double tasks_est = (double)groups * G * N * (double)N;
+  if (tasks_est > 2.0e7) return DASH_ERR_UNSUPPORTED;
+  Problem pb;
+  pb.mask = mask;
+  pb.schedule = schedule;
+  pb.N = N;
+  pb.G = G;
+  pb.groups = groups;
+  pb.P = P;
+  pb.c = c_full;
+  pb.c_diag = c_diag;
+  pb.r = r;
+  const int st = run_problem(pb, dash::closed_form_table(mask, schedule, N, G), dispatch, out);
+  return st == DASH_ERR_TABLE ? DASH_ERR_SCHEDULE_MASK : st;
+}
+
 // The deterministic schedule with the shortest critical path for a shape and
 // worker count: every candidate that applies to the mask and tile count is
 // simulated, deadlocked ones are skipped, and ties go to the earlier
@@ -317,3 +330,27 @@ extern "C" int dash_sim_select(int mask, int N, int G, int groups, int P, int di
   if (out) *out = best_res;
   return DASH_OK;
 }
+
+namespace dash {
+
+int sim_table(int mask, int N, int G, int groups, int P, int dispatch, double c_full, double c_diag, double r,
+              const GroupTable& t, dash_sim_result* out) {
+  if (!out) return DASH_ERR_NULL;
+  if (N < 1 || G < 1 || groups < 1 || P < 1 || (dispatch != 0 && dispatch != 1)) return DASH_ERR_SHAPE;
+  if (mask != MASK_FULL && mask != MASK_CAUSAL) return DASH_ERR_SCHEDULE_MASK;
+  if (!(c_full >= 0.0) || !(c_diag >= 0.0) || !(r >= 0.0)) return DASH_ERR_SHAPE;
+  if ((double)groups * (double)t.tasks.size() > 2.0e7) return DASH_ERR_UNSUPPORTED;
+  Problem pb;
+  pb.mask = mask;
+  pb.schedule = -1;
+  pb.N = N;
+  pb.G = G;
+  pb.groups = groups;
+  pb.P = P;
+  pb.c = c_full;
+  pb.c_diag = c_diag;
+  pb.r = r;
+  return run_problem(pb, t, dispatch, out);
+}
+
+}  // namespace dash

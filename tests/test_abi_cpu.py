@@ -60,7 +60,7 @@ def test_wait_stats_needs_a_workspace():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(10):
         assert dash.dash_status_string(s)
     assert "unknown" in dash.dash_status_string(99)
 
@@ -295,7 +295,9 @@ def test_auto_schedule_arguments():
     L = dash.lib()
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, dash.AUTO) == \
         dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, dash.NAIVE)
-    assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, 6) == 0
+    assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, 7) == 0
+    assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, dash.TABLE) == \
+        dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 1, dash.NAIVE)
     assert L.dash_attn_bwd_auto_schedule(1, 3, 2, 256, 64, 1) == -dash.DASH_ERR_SHAPE
     assert L.dash_attn_bwd_auto_schedule(1, 2, 2, 256, 64, 2) == -dash.DASH_ERR_SCHEDULE_MASK
     assert L.dash_attn_bwd_auto_schedule(0, 2, 2, 256, 64, 1) == dash.NAIVE  # empty
