@@ -49,7 +49,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # the sources the persistent kernel is compiled from
 KERNEL_SOURCES = [os.path.join(ROOT, "scheduling_persistent_attn_amd", "csrc", f)
-                  for f in ("bwd.hip", "bwd_wide.hip", "bwd_common.h", "lds_layout.h", "schedule.h",
+                  for f in ("bwd.hip", "bwd_wide.hip", "bwd_wide64.hip", "bwd_common.h", "lds_layout.h", "schedule.h",
                             "kernels.h")]
 
 

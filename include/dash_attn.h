@@ -111,9 +111,10 @@ enum dash_status {
 };
 
 /* Query-tile and key/value-tile edge T used for a problem (both sides use the
- * same T): for D == 64, 64 when S <= 512, else 128; for D == 128, 128 when
+ * same T): for D == 64, 64 when S <= 512, else 256; for D == 128, 128 when
  * S <= 512, else 256 (a unit then holds the dK/dV of 256 keys, which halves
- * the bytes moved per FLOP).  Returns 0 if D is unsupported. */
+ * the bytes moved per FLOP against 128-key tiles).  Returns 0 if D is
+ * unsupported. */
 int dash_attn_tile_size(int S, int D);
 
 /* Number of parts the query heads of each (batch, key/value head) group are
@@ -384,7 +385,8 @@ int dash_sim_select(int mask, int N, int G, int groups, int P, int dispatch,
  * Deadlock freedom on P workgroups (dash_schedule_table_check): the waits-for
  * graph of the kernels' pipelined hand-offs -- within a run the turn of pass
  * n is taken after pass n+1 and the slice published in pass n+3 (passes per
- * task: 8 for 256-key tiles, 4 for 128-key tiles at D = 128, 2 otherwise) --
+ * task: 8 for 256-key tiles at D = 128, 4 for 256-key tiles at D = 64 and
+ * for 128-key tiles, 2 for 64-key tiles) --
  * has no cycle, and the items split into consecutive dispatch blocks of at
  * most P items where no item waits on a later block.
  */

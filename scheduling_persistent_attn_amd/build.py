@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdash_attn.so")
-SOURCES = ["bwd.hip", "bwd_wide.hip", "fwd.hip", "api.cpp", "sim.cpp", "table.cpp"]
+SOURCES = ["bwd.hip", "bwd_wide.hip", "bwd_wide64.hip", "fwd.hip", "api.cpp", "sim.cpp", "table.cpp"]
 HOST_ONLY = {"sim.cpp", "table.cpp"}  # plain C++, no HIP
 ARCH = "gfx950"
 
@@ -34,7 +34,8 @@ COMMON = [
 # dQ partial sum is loaded straight into its accumulator), and pins the
 # operands it holds for a whole KV tile to the accumulation registers itself
 EXTRA = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "bwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "bwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "bwd_wide64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():
@@ -47,7 +48,7 @@ def hipcc():
 # The debug build with the per-task trace (DASH_TASK_TRACE): the sources that
 # read the flag are compiled again with it and linked into a second library.
 TRACE_LIB = os.path.join(HERE, "libdash_attn_trace.so")
-TRACED = ("bwd.hip", "bwd_wide.hip", "api.cpp")
+TRACED = ("bwd.hip", "bwd_wide.hip", "bwd_wide64.hip", "api.cpp")
 
 
 def build(verbose=False):

@@ -24,7 +24,7 @@ struct DeviceInfo {
   int cus = 0;
   long long wall_khz = 0;
   int bpc[2][2][2] = {};  // [D==128][T==128][causal] resident blocks per CU
-  int bpc_wide[2] = {};   // [causal] of the 256-key tile kernel
+  int bpc_wide[2][2] = {};  // [D==128][causal] of the 256-key tile kernels
 };
 
 DeviceInfo g_dev[kMaxDevices];
@@ -43,12 +43,16 @@ int device_info(DeviceInfo** out) {
       khz = 100000;
     d.cus = cus;
     d.wall_khz = khz;
-    const int cfgs[3][2] = {{64, 64}, {64, 128}, {128, 128}};
+    // the 64- and 128-key tile kernels (larger problems use the 256-key tiles)
+    const int cfgs[2][2] = {{64, 64}, {128, 128}};
     for (auto& cfg : cfgs)
       for (int causal = 0; causal < 2; ++causal)
         d.bpc[cfg[0] == 128][cfg[1] == 128][causal] =
             dash::bwd_blocks_per_cu(cfg[0], cfg[1], causal != 0);
-    for (int causal = 0; causal < 2; ++causal) d.bpc_wide[causal] = dash::bwd_wide_blocks_per_cu(causal != 0);
+    for (int causal = 0; causal < 2; ++causal) {
+      d.bpc_wide[1][causal] = dash::bwd_wide_blocks_per_cu(causal != 0);
+      d.bpc_wide[0][causal] = dash::bwd_wide64_blocks_per_cu(causal != 0);
+    }
     d.ready = true;
   }
   *out = &d;
@@ -59,7 +63,7 @@ inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Persistent workgroups the backward kernel for tile T runs per compute unit.
 int blocks_per_cu(const DeviceInfo& d, int D, int T, int mask) {
-  if (T == 256) return d.bpc_wide[mask];
+  if (T == 256) return d.bpc_wide[D == 128][mask];
   return d.bpc[D == 128][T == 128][mask];
 }
 
@@ -272,7 +276,7 @@ int dash_attn_bwd_head_parts(int B, int Hq, int Hkv, int S, int D, int mask, int
 }
 
 int dash_attn_tile_size(int S, int D) {
-  if (D == 64) return S <= 512 ? 64 : 128;
+  if (D == 64) return S <= 512 ? 64 : 256;
   if (D == 128) return S <= 512 ? 128 : 256;
   return 0;
 }
@@ -501,8 +505,12 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
 int launch_main_phase(const BwdPlan& P, int D, int mask, hipStream_t s) {
   const bool causal = mask == DASH_MASK_CAUSAL;
   if (P.L.T == 256) {
-    if (dash::launch_bwd_wide(causal, P.bp, P.grid, s) != hipSuccess) return DASH_ERR_HIP;
-    if (P.bp.schedule == DASH_SCHED_ATOMIC && dash::launch_finalize_wide(P.fp, s) != hipSuccess)
+    const bool d128 = D == 128;
+    if ((d128 ? dash::launch_bwd_wide(causal, P.bp, P.grid, s) : dash::launch_bwd_wide64(causal, P.bp, P.grid, s)) !=
+        hipSuccess)
+      return DASH_ERR_HIP;
+    if (P.bp.schedule == DASH_SCHED_ATOMIC &&
+        (d128 ? dash::launch_finalize_wide(P.fp, s) : dash::launch_finalize_wide64(P.fp, s)) != hipSuccess)
       return DASH_ERR_HIP;
     if (P.L.parts > 1 && dash::launch_dkv_finalize(P.kp, s) != hipSuccess) return DASH_ERR_HIP;
     return DASH_OK;

@@ -871,7 +871,6 @@ static int blocks_per_cu_impl() {
 
 int bwd_blocks_per_cu(int D, int T, bool causal) {
   if (D == 64 && T == 64) return causal ? blocks_per_cu_impl<64, 64, true>() : blocks_per_cu_impl<64, 64, false>();
-  if (D == 64 && T == 128) return causal ? blocks_per_cu_impl<64, 128, true>() : blocks_per_cu_impl<64, 128, false>();
   if (D == 128 && T == 128) return causal ? blocks_per_cu_impl<128, 128, true>() : blocks_per_cu_impl<128, 128, false>();
   return 0;
 }
@@ -922,7 +921,6 @@ static hipError_t launch_sched(int sched, const BwdParams& p, int grid, hipStrea
 hipError_t launch_bwd_main(int D, int T, bool causal, const BwdParams& p, int grid,
                            hipStream_t s) {
   if (D == 64 && T == 64) return causal ? launch_sched<64, 64, true>(p.schedule, p, grid, s) : launch_sched<64, 64, false>(p.schedule, p, grid, s);
-  if (D == 64 && T == 128) return causal ? launch_sched<64, 128, true>(p.schedule, p, grid, s) : launch_sched<64, 128, false>(p.schedule, p, grid, s);
   if (D == 128 && T == 128) return causal ? launch_sched<128, 128, true>(p.schedule, p, grid, s) : launch_sched<128, 128, false>(p.schedule, p, grid, s);
   return hipErrorInvalidValue;
 }
@@ -933,7 +931,6 @@ hipError_t launch_finalize_atomic(int D, int T, const FinParams& p, hipStream_t 
   if (blocks < 1) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (D == 64 && T == 64) hipLaunchKernelGGL((bwd_finalize<64, 64>), dim3((unsigned)blocks), dim3(256), 0, s, p);
-  else if (D == 64 && T == 128) hipLaunchKernelGGL((bwd_finalize<64, 128>), dim3((unsigned)blocks), dim3(256), 0, s, p);
   else if (D == 128 && T == 128) hipLaunchKernelGGL((bwd_finalize<128, 128>), dim3((unsigned)blocks), dim3(256), 0, s, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();

@@ -54,6 +54,13 @@ __device__ __forceinline__ bf16x8 lds_read_tr(const char* base, int off0, int of
   return a;
 }
 
+// Element e of a packed bf16 fragment into LDS as it sits in its register
+// half (no conversion: the high half goes out with ds_write_b16_d16_hi).
+__device__ __forceinline__ void lds_write_bf16(char* at, const bf16x8& v, int e) {
+  const unsigned pair = __builtin_bit_cast(uint4, v)[e >> 1];
+  *reinterpret_cast<unsigned short*>(at) = (e & 1) ? (unsigned short)(pair >> 16) : (unsigned short)pair;
+}
+
 // ---------------------------------------------------------------------------
 // The ordered hand-off of a dQ slice between workgroups.
 //
@@ -270,6 +277,92 @@ __device__ __forceinline__ void stage_store(const PassStage<D, BQ, NW>& st, char
     *reinterpret_cast<f32x4*>(o_dst + off) = st.o[k];
   }
   if (w < 2 && (BQ == 64 || lane < BQ)) *reinterpret_cast<unsigned*>(l_dst + w * 4 * BQ + lane * 4) = st.l;
+}
+
+// ---------------------------------------------------------------------------
+// Pieces of the 256-key tile kernels (bwd_wide.hip, bwd_wide64.hip): the
+// 16x16x32 product of the dQ slices, the dS block's layout and the slices
+// themselves, all independent of the head dim.
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The dS block has 512-byte rows (32 slots of 16 bytes).  Slot U of row R sits
+// at slot U ^ (R & 15): the 16-byte reads of one slot in 16 consecutive rows
+// (the dQ product's A operand) then touch 16 different groups of four banks.
+__device__ __forceinline__ int ds_phys(int row, int slot) {
+  return row * 512 + ((slot ^ (row & 15)) << 4);
+}
+
+// One wave's 32 x 16 slice of one pass of a dQ tile, and where it goes.
+struct WideSlice {
+  float* acc;     // fp32 accumulator of the slice (512 floats)
+  int* cnt;       // its turn counter
+  int rank;       // position of this contribution in the tile's order
+  int last;       // last contributor: writes bf16 dQ instead of the accumulator
+  int dq_off;     // dq element of (slice row 0, feature 16w + s16)
+  int rows_left;  // rows of the slice that exist: query rows < S, minus 1
+};
+
+struct DQ2 {
+  f32x4 v[2];  // row blocks 0 and 1 (16 rows each)
+};
+
+// Accumulator loads of a slice (device-coherent): element r of row block rb
+// of lane l at float rb*256 + 4l + r, i.e. two fully coalesced 1 KB rows.
+// With nbytes = 0 both loads are out of range and return zeros.
+__device__ __forceinline__ DQ2 wide_acc_load(float* acc, int nbytes, int lane) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(acc, 0, nbytes, 0x00020000);
+  DQ2 v;
+  v.v[0] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, kSC1);
+  v.v[1] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + 1024, 0, kSC1);
+  return v;
+}
+
+// Second half of a slice's reduction: store the new partial sum, or for the
+// last contributor write dQ = scale * sum in bf16.  ATOMIC: unordered fp32
+// atomics instead (element e of lane l at e*64 + l).
+template <bool ATOMIC>
+__device__ __forceinline__ void wide_acc_finish(const WideSlice& sl, const DQ2& dq, int lane, int rs, float scale,
+                                                bf16* gdq, unsigned dq_bytes) {
+  if constexpr (ATOMIC) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) unsafeAtomicAdd(sl.acc + e * 64 + lane, dq.v[e >> 2][e & 3]);
+    return;
+  } else {
+    if (!sl.last) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(sl.acc, 0, 2048, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b128(dq.v[0], r, lane * 16, 0, kSC1);
+      __builtin_amdgcn_raw_buffer_store_b128(dq.v[1], r, lane * 16 + 1024, 0, kSC1);
+    } else {
+      // dq rows 16(e/4) + 4(l/16) + e%4 of the slice, feature 16w + l%16; the
+      // row stride stays opaque so that the per-element offsets are formed
+      // here, not hoisted out of the loop into registers
+      asm volatile("" : "+s"(rs));
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(gdq, 0, (int)dq_bytes, 0x00020000);
+      const int vo = (sl.dq_off + 4 * (lane >> 4) * rs) * 2;
+      if (sl.rows_left >= 31) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bf16 v = (bf16)(dq.v[e >> 2][e & 3] * scale);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, vo,
+                                                (16 * (e >> 2) + (e & 3)) * rs * 2, 0);
+        }
+      } else {
+        // partial last tile: rows past S are not written
+        const int r0 = 4 * (lane >> 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ql = 16 * (e >> 2) + r0 + (e & 3);
+          const bf16 v = (bf16)(dq.v[e >> 2][e & 3] * scale);
+          if (ql <= sl.rows_left)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, vo,
+                                                  (16 * (e >> 2) + (e & 3)) * rs * 2, 0);
+        }
+      }
+    }
+  }
 }
 
 // Publishes rank + 1 on a slice's counter.  The caller has waited for this

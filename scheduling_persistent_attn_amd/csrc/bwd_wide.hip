@@ -39,10 +39,6 @@
 
 namespace dash {
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 struct WideCfg {
   static constexpr int D = 128, T = 256;
   static constexpr int NW = 8;          // waves; wave w owns keys [32w, 32w+32)
@@ -67,13 +63,6 @@ struct WideCfg {
   static_assert(FQ == 16 && SLICE == 512, "one 32 x 16 dQ slice per wave and pass");
 };
 
-// The dS block has 512-byte rows (32 slots of 16 bytes).  Slot U of row R sits
-// at slot U ^ (R & 15): the 16-byte reads of one slot in 16 consecutive rows
-// (the dQ product's A operand) then touch 16 different groups of four banks.
-__device__ __forceinline__ int ds_phys(int row, int slot) {
-  return row * 512 + ((slot ^ (row & 15)) << 4);
-}
-
 // Per-lane LDS byte offsets of the wide kernel (see LaneOffs in bwd.hip for
 // the idea: every access pattern is a per-lane base XOR or plus a constant).
 struct WideOffs {
@@ -93,76 +82,6 @@ struct WideOffs {
   static constexpr int wy(int x) { return (8 * (x >> 2) + (x & 3)) * 512; }
   __device__ __forceinline__ int W(int x) const { return (wr ^ wx(x)) + wy(x); }
 };
-
-// One wave's 32 x 16 slice of one pass of a dQ tile, and where it goes.
-struct WideSlice {
-  float* acc;     // fp32 accumulator of the slice (512 floats)
-  int* cnt;       // its turn counter
-  int rank;       // position of this contribution in the tile's order
-  int last;       // last contributor: writes bf16 dQ instead of the accumulator
-  int dq_off;     // dq element of (slice row 0, feature 16w + s16)
-  int rows_left;  // rows of the slice that exist: query rows < S, minus 1
-};
-
-struct DQ2 {
-  f32x4 v[2];  // row blocks 0 and 1 (16 rows each)
-};
-
-// Accumulator loads of a slice (device-coherent): element r of row block rb
-// of lane l at float rb*256 + 4l + r, i.e. two fully coalesced 1 KB rows.
-// With nbytes = 0 both loads are out of range and return zeros.
-__device__ __forceinline__ DQ2 wide_acc_load(float* acc, int nbytes, int lane) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(acc, 0, nbytes, 0x00020000);
-  DQ2 v;
-  v.v[0] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, kSC1);
-  v.v[1] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + 1024, 0, kSC1);
-  return v;
-}
-
-// Second half of a slice's reduction: store the new partial sum, or for the
-// last contributor write dQ = scale * sum in bf16.  ATOMIC: unordered fp32
-// atomics instead (element e of lane l at e*64 + l).
-template <bool ATOMIC>
-__device__ __forceinline__ void wide_acc_finish(const WideSlice& sl, const DQ2& dq, int lane, int rs, float scale,
-                                                bf16* gdq, unsigned dq_bytes) {
-  if constexpr (ATOMIC) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) unsafeAtomicAdd(sl.acc + e * 64 + lane, dq.v[e >> 2][e & 3]);
-    return;
-  } else {
-    if (!sl.last) {
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(sl.acc, 0, 2048, 0x00020000);
-      __builtin_amdgcn_raw_buffer_store_b128(dq.v[0], r, lane * 16, 0, kSC1);
-      __builtin_amdgcn_raw_buffer_store_b128(dq.v[1], r, lane * 16 + 1024, 0, kSC1);
-    } else {
-      // dq rows 16(e/4) + 4(l/16) + e%4 of the slice, feature 16w + l%16; the
-      // row stride stays opaque so that the per-element offsets are formed
-      // here, not hoisted out of the loop into registers
-      asm volatile("" : "+s"(rs));
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(gdq, 0, (int)dq_bytes, 0x00020000);
-      const int vo = (sl.dq_off + 4 * (lane >> 4) * rs) * 2;
-      if (sl.rows_left >= 31) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bf16 v = (bf16)(dq.v[e >> 2][e & 3] * scale);
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, vo,
-                                                (16 * (e >> 2) + (e & 3)) * rs * 2, 0);
-        }
-      } else {
-        // partial last tile: rows past S are not written
-        const int r0 = 4 * (lane >> 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ql = 16 * (e >> 2) + r0 + (e & 3);
-          const bf16 v = (bf16)(dq.v[e >> 2][e & 3] * scale);
-          if (ql <= sl.rows_left)
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, vo,
-                                                  (16 * (e >> 2) + (e & 3)) * rs * 2, 0);
-        }
-      }
-    }
-  }
-}
 
 // dQ slice of one pass: rows 0..31 of the pass x features 16w .. 16w+15, over
 // the 256 keys of the tile; A = dS rows (LDS), B = K^T (transposing reads of
@@ -224,7 +143,7 @@ __device__ __forceinline__ void wide_dvdk(const char* lQ, const char* lO, const 
 #pragma unroll
     for (int e = 0; e < WPS; ++e) {
       const int r = x * WPS + e;
-      *reinterpret_cast<bf16*>(lS + o.W(r & 7) + (r >> 3) * 16 * C::RBS) = dsb[r >> 3][r & 7];
+      lds_write_bf16(lS + o.W(r & 7) + (r >> 3) * 16 * C::RBS, dsb[r >> 3], r & 7);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -303,6 +222,9 @@ __device__ __forceinline__ void wide_pass(const char* lQ, const char* lO, const 
   // ---- softmax, then dV^T += dO^T P, dK^T += Q^T dS; dS -> LDS
   bf16x8 pb[2], dsb[2];
   wide_softmax(sa, pa, scale_log2e, pb, dsb);
+  // the dS element writes take the bf16 halves of these registers as they
+  // are, instead of converting every element once more
+  asm volatile("" : "+v"(dsb[0]), "+v"(dsb[1]));
   wide_dvdk(lQ, lO, o, pb, dsb, dK, dV, lS_cur);
 
   // ---- dQ of the slice two passes back on its loaded partial sum

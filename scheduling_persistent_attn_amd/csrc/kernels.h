@@ -129,6 +129,11 @@ int bwd_wide_blocks_per_cu(bool causal);
 hipError_t launch_bwd_wide(bool causal, const BwdParams& p, int grid, hipStream_t s);
 hipError_t launch_finalize_wide(const FinParams& p, hipStream_t s);
 
+// The 256-key tile kernel for head dim 64 (bwd_wide64.hip).
+int bwd_wide64_blocks_per_cu(bool causal);
+hipError_t launch_bwd_wide64(bool causal, const BwdParams& p, int grid, hipStream_t s);
+hipError_t launch_finalize_wide64(const FinParams& p, hipStream_t s);
+
 hipError_t launch_dkv_finalize(const DkvFinParams& p, hipStream_t s);
 
 hipError_t launch_preprocess(const PreParams& p, hipStream_t s);

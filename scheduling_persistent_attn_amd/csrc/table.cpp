@@ -255,7 +255,7 @@ GroupTable closed_form_table(int mask, int schedule, int N, int G) {
 // (one pass = the rows of a query tile that the workgroup's waves cover
 // together: 32 rows when the waves split the head dim, else 64).
 int passes_per_task(int T, int D) {
-  if (T == 256) return 8;
+  if (T == 256) return D == 128 ? 8 : 4;  // 32-row passes at D = 128, 64-row at 64
   const int NW = T / 32, DB = D / 32;
   return T / (32 * (NW / DB));
 }

@@ -67,16 +67,17 @@ def test_status_strings():
 
 def test_tile_and_workspace_size():
     assert dash.dash_attn_tile_size(256, 64) == 64
-    assert dash.dash_attn_tile_size(4096, 64) == 128
+    assert dash.dash_attn_tile_size(4096, 64) == 256
+    assert dash.dash_attn_tile_size(513, 64) == 256
     assert dash.dash_attn_tile_size(512, 128) == 128
     assert dash.dash_attn_tile_size(513, 128) == 256
     assert dash.dash_attn_tile_size(4096, 128) == 256
     assert dash.dash_attn_tile_size(100, 96) == 0
     # one turn counter per slice a wave reduces per pass: 32 x 32 for tiles of
-    # 64 and 128, 32 x 16 for 256
+    # 64 and 128, 32 x 16 for 256 (both head dims)
     for (B, Hq, Hkv, S, D, T, per_tile) in ((4, 32, 8, 4096, 128, 256, 256 * 128 // 512),
                                             (2, 8, 4, 512, 128, 128, 128 * 128 // 1024),
-                                            (2, 24, 24, 4096, 64, 128, 128 * 64 // 1024)):
+                                            (2, 24, 24, 4096, 64, 256, 256 * 64 // 512)):
         N = (S + T - 1) // T
         n = dash.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, D, 1, 2)
         rows = B * Hq * N * T
@@ -309,8 +310,9 @@ def test_auto_schedule_arguments():
 
 def test_sim_report_closed_forms(capsys):
     """bench.py --sim-report on the large workloads; two cases have closed
-    forms.  dit_full at P = 256, r = 0: 48 groups x 32 chains of 32 unit tasks
-    on 256 workers are 6 rounds of 32, so every schedule's critical path is 192.
+    forms.  dit_full at P = 256, r = 0, with 256-key tiles (N = 16): 48 groups
+    x 16 chains of 16 unit tasks on 256 workers are 3 rounds of 16, so every
+    schedule's critical path is 48.
     llama8b_causal, symmetric shift, P = 256, r = 0, with 256-key tiles (N =
     16): 32 groups x 8 pairs of 17 tasks for each of 4 query heads (68 per
     item) in one round: 68, with efficiency 1 and no Lemma 1 violation."""
@@ -322,7 +324,8 @@ def test_sim_report_closed_forms(capsys):
     assert len(rows) == 84
     pick = {(r["workload"], r["P"], r["r_over_c"], r["schedule"]): r for r in rows}
     for s in ("naive", "descending_q", "shift"):
-        assert pick[("dit_full", 256, 0.0, s)]["critical_path"] == 192.0
+        assert pick[("dit_full", 256, 0.0, s)]["critical_path"] == 48.0
+    assert dash.dash_attn_tile_size(4096, 64) == 256
     sym = pick[("llama8b_causal", 256, 0.0, "symmetric_shift")]
     assert dash.dash_attn_tile_size(4096, 128) == 256
     assert sym["critical_path"] == 68.0 and sym["lemma1_violations"] == 0
@@ -405,9 +408,11 @@ def test_head_parts_rule():
     # small shapes take every divisor up to G
     assert hp(1, 4, 2, 1024, 128, 1, dash.NAIVE) == 2
     assert hp(1, 6, 1, 1024, 128, 0, dash.SHIFT) == 6
-    # 128-key tiles and single-head groups are never split
+    # 256-key tiles at head dim 64 split the same way
+    assert hp(1, 8, 2, 4096, 64, 1, dash.NAIVE) == 4
+    # 64- and 128-key tiles and single-head groups are never split
     assert hp(1, 8, 2, 512, 128, 1, dash.NAIVE) == 1
-    assert hp(1, 8, 2, 4096, 64, 1, dash.NAIVE) == 1
+    assert hp(1, 8, 2, 512, 64, 1, dash.NAIVE) == 1
     assert hp(1, 8, 8, 4096, 128, 1, dash.NAIVE) == 1
     assert hp(1, 3, 2, 4096, 128, 1, dash.NAIVE) == 0  # invalid
 

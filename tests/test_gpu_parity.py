@@ -33,7 +33,7 @@ CASES = [
     (1, 300, 2, 1, 64, False),    # partial last tile (T = 64, N = 5)
     (1, 300, 2, 2, 64, True),
     (1, 450, 3, 1, 128, True),    # partial last tile, N = 4, G = 3
-    (1, 1024, 2, 1, 64, True),    # D = 64 with 128 tiles, N = 8
+    (1, 1024, 2, 1, 64, True),    # D = 64 with 256-key tiles, N = 4
     (1, 1, 2, 1, 64, True),       # single token
     (1, 64, 1, 1, 128, False),    # single partial tile
     (2, 512, 8, 4, 64, True),     # 8 (batch, kv head) groups: one item queue per XCD
@@ -43,6 +43,10 @@ CASES = [
     (2, 768, 4, 4, 128, True),    # 256-key tiles, N = 3 (no symmetric shift)
     (1, 2048, 2, 2, 128, True),   # 256-key tiles, N = 8
     (1, 700, 3, 1, 128, True),    # 256-key tiles, partial last tile, G = 3
+    (1, 1100, 2, 1, 64, False),   # D = 64, 256-key tiles, partial last tile (N = 5)
+    (2, 2048, 4, 2, 64, True),    # D = 64, 256-key tiles, N = 8, GQA groups of 2
+    (1, 700, 3, 1, 64, True),     # D = 64, 256-key tiles, partial last tile, G = 3
+    (1, 4096, 2, 2, 64, False),   # D = 64, 256-key tiles, N = 16
 ]
 
 

@@ -41,7 +41,7 @@ def _same(a, b):
 CLOSED = [
     # B, S, Hq, Hkv, D, causal -- one case per kernel tile and both masks
     (1, 256, 2, 1, 64, True),     # T = 64
-    (2, 1024, 4, 2, 64, False),   # D = 64, T = 128
+    (2, 1024, 4, 2, 64, False),   # D = 64, T = 256
     (1, 512, 4, 2, 128, True),    # D = 128, T = 128
     (1, 2048, 2, 2, 128, False),  # T = 256
     (1, 2048, 4, 1, 128, True),   # T = 256, G = 4 (closed forms split the heads)
@@ -78,8 +78,8 @@ SEARCHED = [
     # B, S, Hq, Hkv, D, causal, grid
     (1, 2048, 2, 1, 128, False, 3),   # T = 256, N = 8 chains on 3 workgroups
     (1, 2048, 4, 2, 128, True, 2),    # T = 256, N = 8, two groups of G = 2
-    (1, 2048, 2, 2, 64, False, 4),    # D = 64, T = 128, N = 16
-    (1, 1900, 2, 1, 64, True, 5),     # ragged last tile, N = 15
+    (1, 4096, 2, 2, 64, False, 4),    # D = 64, T = 256, N = 16
+    (1, 1900, 2, 1, 64, True, 5),     # D = 64, ragged last tile, N = 8
     (2, 512, 4, 2, 128, True, 2),     # D = 128, T = 128, N = 4
 ]
 
@@ -158,13 +158,13 @@ def _sentinel_outputs(x):
 
 
 def test_kernel_refuses_a_table_for_another_kernel():
-    # same N and G, packed for D = 64 (2 passes per task), launched at D = 128
+    # same N and G, packed for D = 64 (4 passes per task), launched at D = 128
     # (8 passes): the sizes agree, the header does not
     B, S, Hq, Hkv, D, causal = 1, 4096, 2, 1, 128, False
     T, N = _tiles(S, D)
-    assert _tiles(2048, 64)[1] == N
+    assert _tiles(S, 64)[1] == N
     offs, tasks = dash.dash_schedule_table_closed_form(0, dash.NAIVE, N, 2)
-    raw = dash.dash_schedule_table_pack(2048, 64, 0, 2, offs, tasks)
+    raw = dash.dash_schedule_table_pack(S, 64, 0, 2, offs, tasks)
     table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).cuda()
     x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=5300)
     o, lse = gu.run_forward(x, causal)

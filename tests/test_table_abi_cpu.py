@@ -21,7 +21,7 @@ def _lists(offs, tasks):
 
 
 # (S, D) -> (N, passes per task) of the kernel that runs it
-SHAPES = {(256, 64): (4, 2), (512, 64): (8, 2), (1024, 64): (8, 2), (384, 128): (3, 4),
+SHAPES = {(256, 64): (4, 2), (512, 64): (8, 2), (1024, 64): (4, 4), (384, 128): (3, 4),
           (512, 128): (4, 4), (768, 128): (3, 8), (1024, 128): (4, 8), (1536, 128): (6, 8),
           (2048, 128): (8, 8), (4096, 128): (16, 8)}
 
