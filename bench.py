@@ -114,6 +114,15 @@ def algorithmic_bytes(cfg, T, parts=1):
     return tasks * per_task + handoff + dq_out + kv
 
 
+def dq_partial_adds(cfg, T):
+    """fp32 element additions into the dQ accumulator per launch: every task
+    adds its T x D contribution (whole tiles)."""
+    B, S, Hq, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["D"]
+    N = (S + T - 1) // T
+    tasks = B * Hq * (N * (N + 1) // 2 if cfg["causal"] else N * N)
+    return tasks * T * D
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -339,7 +348,9 @@ def sim_report():
     large workload, from the library's simulator: P = 256 workers (the
     compute units of an MI355X) and 132 (the SM count of the H800 the pages
     measure on), dynamic dispatch, c = c_diag = 1, r/c in {0, 0.1, 0.25}.
-    One line of JSON per case."""
+    Each schedule runs with the query-head split the library gives it (a
+    split group simulates as `parts` groups of G / parts heads, in the same
+    dispatch order).  One line of JSON per case."""
     import scheduling_persistent_attn_amd as dash
     names = {v: k for k, v in dash.SCHEDULES.items()}
     for name in ("llama8b_causal", "dit_full", "long_full", "qwen7b_causal"):
@@ -354,8 +365,11 @@ def sim_report():
                 for sched in (dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT, dash.SYMMETRIC_SHIFT):
                     if sched == dash.SYMMETRIC_SHIFT and (not mask or N % 2):
                         continue
-                    res = dash.dash_sim_run(mask, sched, N, G, groups, P, 1, 1.0, 1.0, r)
+                    parts = dash.dash_attn_bwd_head_parts(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"],
+                                                          cfg["D"], mask, sched)
+                    res = dash.dash_sim_run(mask, sched, N, G // parts, groups * parts, P, 1, 1.0, 1.0, r)
                     print(json.dumps({"workload": name, "N": N, "G": G, "groups": groups,
+                                      "head_parts": parts,
                                       "P": P, "r_over_c": r, "schedule": names[sched],
                                       "critical_path": res["makespan"],
                                       "efficiency": res["efficiency"],
