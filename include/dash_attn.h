@@ -138,7 +138,9 @@ int dash_attn_bwd_head_parts(int B, int Hq, int Hkv, int S, int D, int mask, int
  *                          number of waits that timed out, [3] always
  *                          zero, [4] set when a run found the workspace not
  *                          prepared, [5] set when the kernel refused a task
- *                          table (dash_attn_bwd_table), [8..15]
+ *                          table (dash_attn_bwd_table), [6] set when a
+ *                          per-head table wrote its fp32 dK/dV partials,
+ *                          [8..15]
  *                          four uint64: shader-clock and 100 MHz-clock
  *                          stamps of workgroup 0 at the persistent kernel's
  *                          start and exit (their ratio is the clock it ran at)
@@ -368,7 +370,8 @@ int dash_sim_select(int mask, int N, int G, int groups, int P, int dispatch,
  * above are members of the family searched here.
  *
  * A table describes one (batch, key/value head) group; every group runs it.
- *   items          number of items (1..N): what a workgroup takes at a time
+ *   items          number of items (1..N, 1..G*N in the per-head form below):
+ *                  what a workgroup takes at a time
  *   item_offsets   items + 1 ints: item k is tasks item_offsets[k] ..
  *                  item_offsets[k+1] - 1, item_offsets[0] = 0, strictly
  *                  increasing, item_offsets[items] = number of tasks
@@ -379,8 +382,12 @@ int dash_sim_select(int mask, int N, int G, int groups, int P, int dispatch,
  * Valid when every unmasked (g, i, j) appears exactly once, the ranks of each
  * dQ tile are a permutation, and all tasks of a key/value tile (every head
  * and query tile) form one unbroken run inside one item (the unit keeps its
- * dK/dV in registers, section 2.1).  Tasks run in item order; dispatch gives
- * items to workgroups in order, group by group.
+ * dK/dV in registers, section 2.1) -- or, in the per-head form, all tasks of
+ * each (head, key/value tile) do: then each run's dK/dV leave the unit as
+ * that head's fp32 partial and a fixed-order pass adds the G partials of each
+ * key row (256-key tiles only; the workspace of DASH_SCHED_TABLE covers them).
+ * The whole-tile form is taken when both hold.  Tasks run in item order;
+ * dispatch gives items to workgroups in order, group by group.
  *
  * Deadlock freedom on P workgroups (dash_schedule_table_check): the waits-for
  * graph of the kernels' pipelined hand-offs -- within a run the turn of pass
@@ -397,7 +404,10 @@ enum dash_family {
   DASH_FAMILY_SHIFT = 1,      /* cyclic walk from the diagonal (causal: the
                                  diagonal upward)                            */
   DASH_FAMILY_DESCENDING = 2, /* query tiles from the last down              */
-  DASH_FAMILY_ASCENDING = 3   /* query tiles from the first up (full masks)  */
+  DASH_FAMILY_ASCENDING = 3,  /* query tiles from the first up (full masks)  */
+  DASH_FAMILY_PACKED = 4      /* (head, key/value tile) chains packed longest
+                                 first into one item per workgroup; reduced
+                                 in the order of their no-wait start        */
 };
 
 /* Tasks in one group's table: G * N * N (full) or G * N(N+1)/2 (causal);
@@ -408,6 +418,14 @@ long long dash_schedule_table_tasks(int mask, int N, int G);
  * a table; item_offsets needs N + 1 ints, tasks 4 ints per task. */
 int dash_schedule_table_closed_form(int mask, int schedule, int N, int G, int* items,
                                     int* item_offsets, int* tasks);
+
+/* One member of the searched family (below) as a table: kind, order (0
+ * ascending, 1 descending; the packed kind has order 0 only) and block
+ * (dispatch block size in units, or the packed kind's bins).  item_offsets
+ * needs G * N + 1 ints, tasks 4 ints per task.  DASH_ERR_SCHEDULE_MASK if the
+ * kind does not apply to the mask and N. */
+int dash_schedule_table_family(int mask, int N, int G, int kind, int order, int block, int* items,
+                               int* item_offsets, int* tasks);
 
 /* DASH_OK if the table is valid for tiles of dash_attn_tile_size(S, D) and
  * deadlock free on P workgroups, DASH_ERR_TABLE if not; DASH_ERR_UNSUPPORTED
@@ -434,7 +452,8 @@ int dash_sim_table(int mask, int N, int G, int groups, int P, int dispatch, doub
 /* Search over a family of block-wise lockstep walks for the shortest
  * simulated critical path (dynamic dispatch, `groups` groups on P
  * workgroups, weights as in dash_sim_run).  Candidates, in tie-break order:
- * each family kind that applies (SYMMETRIC, SHIFT, DESCENDING, ASCENDING),
+ * each family kind that applies (SYMMETRIC, SHIFT, DESCENDING, ASCENDING,
+ * PACKED; PACKED with G > 1 only for 256-key tiles),
  * units (chains, or symmetric pairs) in ascending then descending order, and
  * dispatch blocks of min(units, P), half that, and 1 consecutive units; dQ
  * tile (g, j) is reduced in the order (block, step at which the unit reaches
@@ -442,9 +461,12 @@ int dash_sim_table(int mask, int N, int G, int groups, int P, int dispatch, doub
  * ascending, one block), so the result is never worse than the best closed
  * form that runs on P workgroups, and the family reaches N > P, where the
  * shift family cannot run.  Candidates that fail dash_schedule_table_check
- * on P are skipped.  Writes the winner (item_offsets: N + 1 ints, tasks: 4
- * ints per task), family = {kind, order (0 ascending), block} (may be NULL)
- * and its report (may be NULL). */
+ * on P are skipped.  The packed kind (one order, `block` = its bins: the
+ * workgroups one group gets, min(G * N, P / groups)) reaches beyond the
+ * walks when equal chains leave workgroups idle at the end, e.g. a last
+ * round of items for part of the grid.  Writes the winner (item_offsets:
+ * G * N + 1 ints, tasks: 4 ints per task), family = {kind, order (0
+ * ascending), block} (may be NULL) and its report (may be NULL). */
 int dash_schedule_search(int S, int D, int mask, int G, int groups, int P, double c_full,
                          double c_diag, double r, int* items, int* item_offsets, int* tasks,
                          int* family, dash_sim_result* out);

@@ -27,6 +27,16 @@ holds the closed forms of section 2.2 as members):
   blocks of min(units, P), half that and 1; the shortest simulated critical
   path (oracle.dag, dynamic dispatch) wins, ties to the earlier candidate.
 
+A fifth kind, PACKED, drops the lockstep walk for load balance: each
+(head, KV tile) is a chain of its own (walk as SHIFT), chains go longest first
+to the least loaded of `bins` bins (lowest bin on ties; bins = the workgroups
+one group gets, min(G*N, P // groups)), the non-empty bins in order are the
+items, and dQ tile (g, j) is reduced in the order (position of the task in its
+item, item).  With G > 1 the chains of one KV tile then sit in different
+items: a table in the per-head form, where each (head, KV tile)'s tasks are
+one run (its dK/dV leave the unit as that head's partial); tables whose KV
+tiles each form one run are in the whole-tile form, taken when both hold.
+
 Deadlock freedom.  A table is run by persistent workgroups that take items in
 order and keep them; a dQ hand-off waits for the previous rank.  The kernels
 pipeline each hand-off: within a key/value tile's run, in pass m the turn of
@@ -44,7 +54,7 @@ Tables are (offs, tasks): item k is tasks[offs[k]:offs[k+1]], a task is
 from . import dag
 from . import schedule as sch
 
-SYMMETRIC, SHIFT, DESCENDING, ASCENDING = 0, 1, 2, 3
+SYMMETRIC, SHIFT, DESCENDING, ASCENDING, PACKED = 0, 1, 2, 3, 4
 
 
 def tiles(mask, N):
@@ -61,11 +71,42 @@ def closed_form_table(schedule, mask, N, G=1):
     return offs, tasks
 
 
+def run_key(task, split):
+    g, i = task[0], task[1]
+    return (g, i) if split else i
+
+
+def one_run_each(offs, tasks, split):
+    """Whether every run key occurs in one unbroken stretch of one item."""
+    seen = set()
+    for k in range(len(offs) - 1):
+        prev = None
+        for t in tasks[offs[k]:offs[k + 1]]:
+            key = run_key(t, split)
+            if key != prev:
+                if key in seen:
+                    return False
+                seen.add(key)
+                prev = key
+    return True
+
+
+def table_form(offs, tasks):
+    """'tile' (each KV tile one run), else 'head' (each (head, KV tile) one
+    run), else None."""
+    if one_run_each(offs, tasks, False):
+        return "tile"
+    if one_run_each(offs, tasks, True):
+        return "head"
+    return None
+
+
 def structure_ok(mask, N, G, offs, tasks):
     """Every unmasked (g, i, j) exactly once; ranks of each dQ tile a
-    permutation; each KV tile's tasks one contiguous run inside one item."""
+    permutation; each KV tile's tasks one contiguous run inside one item, or
+    each (head, KV tile)'s tasks."""
     items = len(offs) - 1
-    if items < 1 or items > N or offs[0] != 0 or offs[-1] != len(tasks):
+    if items < 1 or items > G * N or offs[0] != 0 or offs[-1] != len(tasks):
         return False
     if any(offs[k + 1] <= offs[k] for k in range(items)):
         return False
@@ -78,26 +119,17 @@ def structure_ok(mask, N, G, offs, tasks):
             rs = sorted(r for (gg, _, jj, r) in tasks if gg == g and jj == j)
             if rs != list(range(len(sch.contributors(mask, N, j)))):
                 return False
-    seen = set()
-    for k in range(items):
-        prev = None
-        for (_, i, _, _) in tasks[offs[k]:offs[k + 1]]:
-            if i != prev:
-                if i in seen:
-                    return False
-                seen.add(i)
-                prev = i
-    return True
+    return table_form(offs, tasks) is not None
 
 
-def runs(offs, tasks):
-    """[(item, first task index, last task index)] of every key/value run."""
+def runs(offs, tasks, split=False):
+    """[(item, first task index, last task index)] of every run."""
     out = []
     for k in range(len(offs) - 1):
         t = offs[k]
         while t < offs[k + 1]:
             u = t
-            while u + 1 < offs[k + 1] and tasks[u + 1][1] == tasks[t][1]:
+            while u + 1 < offs[k + 1] and run_key(tasks[u + 1], split) == run_key(tasks[t], split):
                 u += 1
             out.append((k, t, u))
             t = u + 1
@@ -150,7 +182,7 @@ def dispatch_blocks(offs, tasks):
     return sizes
 
 
-def events_acyclic(offs, tasks, passes):
+def events_acyclic(offs, tasks, passes, split=False):
     """Whether the waits-for graph of the hand-off events has no cycle."""
     succ = {}
     indeg = {}
@@ -167,7 +199,7 @@ def events_acyclic(offs, tasks, passes):
 
     for k in range(len(offs) - 1):
         prev_last = None
-        for (kk, a, b) in runs(offs, tasks):
+        for (kk, a, b) in runs(offs, tasks, split):
             if kk != k:
                 continue
             ev = run_events(a, b, passes)
@@ -197,7 +229,8 @@ def events_acyclic(offs, tasks, passes):
 def protocol_ok(mask, N, offs, tasks, passes, P):
     """(ok, number of dispatch blocks, widest block) on P workgroups."""
     sizes = dispatch_blocks(offs, tasks)
-    ok = max(sizes) <= P and events_acyclic(offs, tasks, passes)
+    split = table_form(offs, tasks) == "head"
+    ok = max(sizes) <= P and events_acyclic(offs, tasks, passes, split)
     return ok, len(sizes), max(sizes)
 
 
@@ -220,10 +253,49 @@ def family_applies(mask, N, kind):
         return mask == sch.CAUSAL and N % 2 == 0
     if kind == ASCENDING:
         return mask == sch.FULL
-    return kind in (SHIFT, DESCENDING)
+    return kind in (SHIFT, DESCENDING, PACKED)
+
+
+def packed_bins(N, G, groups, P):
+    return max(1, min(G * N, P // groups))
+
+
+def packed_table(mask, N, G, bins):
+    """The PACKED kind (module docstring) with `bins` bins."""
+    chains = []
+    for g in range(G):
+        for i in range(N):
+            walk = [j for (_, j) in unit_walk(mask, N, SHIFT, i)]
+            chains.append((-len(walk), g, i, walk))
+    chains.sort(key=lambda c: c[:3])
+    loads = [0] * bins
+    content = [[] for _ in range(bins)]
+    for (neg, g, i, walk) in chains:
+        b = min(range(bins), key=lambda x: (loads[x], x))
+        content[b].append((g, i, walk))
+        loads[b] -= neg
+    item_tasks = []
+    for b in range(bins):
+        if content[b]:
+            item_tasks.append([(g, i, j) for (g, i, walk) in content[b] for j in walk])
+    order = {}
+    for k, lst in enumerate(item_tasks):
+        for pos, (g, i, j) in enumerate(lst):
+            order.setdefault((g, j), []).append((pos, k, i))
+    rank = {}
+    for (g, j), lst in order.items():
+        for r, (_, _, i) in enumerate(sorted(lst)):
+            rank[(g, i, j)] = r
+    offs, tasks = [0], []
+    for lst in item_tasks:
+        tasks.extend((g, i, j, rank[(g, i, j)]) for (g, i, j) in lst)
+        offs.append(len(tasks))
+    return offs, tasks
 
 
 def family_table(mask, N, G, kind, order, block):
+    if kind == PACKED:
+        return packed_table(mask, N, G, block)
     units = N // 2 if kind == SYMMETRIC else N
     seq = list(range(units)) if order == 0 else list(range(units - 1, -1, -1))
     walks = [unit_walk(mask, N, kind, u) for u in seq]
@@ -263,15 +335,21 @@ def simulate_table(mask, N, G, groups, P, offs, tasks, c=1.0, c_diag=None, r=0.0
                         c_diag=c_diag, r=r, rank_map=rank_map, item_lists=item_lists)
 
 
-def search(mask, N, G, groups, P, passes, c=1.0, c_diag=None, r=0.0):
-    """(offs, tasks, (kind, order, block), report) of the best candidate."""
+def search(mask, N, G, groups, P, passes, c=1.0, c_diag=None, r=0.0, head_form_ok=True):
+    """(offs, tasks, (kind, order, block), report) of the best candidate.
+    head_form_ok: whether tables in the per-head form can run (the kernels
+    of 256-key tiles); without it PACKED is tried only for G = 1."""
     best = None
-    for kind in (SYMMETRIC, SHIFT, DESCENDING, ASCENDING):
+    for kind in (SYMMETRIC, SHIFT, DESCENDING, ASCENDING, PACKED):
         if not family_applies(mask, N, kind):
             continue
+        if kind == PACKED and G > 1 and not head_form_ok:
+            continue
         units = N // 2 if kind == SYMMETRIC else N
-        for order in (0, 1):
-            for b in family_blocks(units, P):
+        orders = (0,) if kind == PACKED else (0, 1)
+        blocks = [packed_bins(N, G, groups, P)] if kind == PACKED else family_blocks(units, P)
+        for order in orders:
+            for b in blocks:
                 offs, tasks = family_table(mask, N, G, kind, order, b)
                 if not protocol_ok(mask, N, offs, tasks, passes, P)[0]:
                     continue

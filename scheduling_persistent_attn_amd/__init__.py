@@ -32,7 +32,7 @@ DASH_ERR_NOT_PREPARED = 8
 DASH_ERR_TABLE = 9
 
 # family kinds of dash_schedule_search
-FAMILY_SYMMETRIC, FAMILY_SHIFT, FAMILY_DESCENDING, FAMILY_ASCENDING = 0, 1, 2, 3
+FAMILY_SYMMETRIC, FAMILY_SHIFT, FAMILY_DESCENDING, FAMILY_ASCENDING, FAMILY_PACKED = 0, 1, 2, 3, 4
 
 SYMBOLS = (
     "dash_attn_tile_size", "dash_attn_bwd_workspace_size", "dash_attn_fwd",
@@ -41,7 +41,8 @@ SYMBOLS = (
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
     "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog", "dash_attn_bwd_wait_stats",
     "dash_attn_bwd_noalloc", "dash_attn_bwd_head_parts",
-    "dash_schedule_table_tasks", "dash_schedule_table_closed_form", "dash_schedule_table_check",
+    "dash_schedule_table_tasks", "dash_schedule_table_closed_form", "dash_schedule_table_family",
+    "dash_schedule_table_check",
     "dash_schedule_table_pack", "dash_sim_table", "dash_schedule_search", "dash_attn_bwd_table",
 )
 
@@ -138,6 +139,8 @@ def _load(path):
     L.dash_schedule_table_tasks.restype = ctypes.c_longlong
     L.dash_schedule_table_closed_form.argtypes = [i] * 4 + [ip, ip, ip]
     L.dash_schedule_table_closed_form.restype = i
+    L.dash_schedule_table_family.argtypes = [i] * 6 + [ip, ip, ip]
+    L.dash_schedule_table_family.restype = i
     L.dash_schedule_table_check.argtypes = [i] * 6 + [ip, ip]
     L.dash_schedule_table_check.restype = i
     L.dash_schedule_table_pack.argtypes = [i] * 5 + [ip, ip, p, sz, ip]
@@ -241,9 +244,9 @@ def _iptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
 
 
-def _table_out(n_tasks, N):
+def _table_out(n_tasks, max_items):
     import numpy as np
-    return np.zeros(N + 1, dtype=np.int32), np.zeros((n_tasks, 4), dtype=np.int32)
+    return np.zeros(max_items + 1, dtype=np.int32), np.zeros((n_tasks, 4), dtype=np.int32)
 
 
 def dash_schedule_table_tasks(mask, N, G):
@@ -261,6 +264,22 @@ def dash_schedule_table_closed_form(mask, schedule, N, G):
                                                ctypes.byref(items), _iptr(offs), _iptr(tasks))
     if st != DASH_OK:
         raise DashError(st, "dash_schedule_table_closed_form")
+    return offs[:items.value + 1], tasks
+
+
+def dash_schedule_table_family(mask, N, G, kind, order, block):
+    """One member of the searched family as a table: (item_offsets, tasks)."""
+    if order == 1 and kind == FAMILY_PACKED:
+        raise ValueError("the packed kind has order 0 only")
+    n = dash_schedule_table_tasks(mask, N, G)
+    if n < 0:
+        raise ValueError("invalid mask, N or G")
+    offs, tasks = _table_out(n, G * N)
+    items = ctypes.c_int()
+    st = lib().dash_schedule_table_family(int(mask), int(N), int(G), int(kind), int(order), int(block),
+                                          ctypes.byref(items), _iptr(offs), _iptr(tasks))
+    if st != DASH_OK:
+        raise DashError(st, "dash_schedule_table_family")
     return offs[:items.value + 1], tasks
 
 
@@ -316,7 +335,7 @@ def dash_schedule_search(S, D, mask, G=1, groups=1, P=256, c_full=1.0, c_diag=No
     n = dash_schedule_table_tasks(mask, N, G)
     if n < 0:
         raise ValueError("invalid mask or G")
-    offs, tasks = _table_out(n, N)
+    offs, tasks = _table_out(n, G * N)
     items = ctypes.c_int()
     fam = (ctypes.c_int * 3)()
     out = SimResult()

@@ -100,8 +100,10 @@ constexpr int kSplitTargetItems = 256;
 // largest over the schedules it can resolve to (the workspace then covers
 // any of them).
 int head_parts(int B, int Hkv, int G, int N, int T, int mask, int schedule) {
-  // a table keeps every key/value tile's heads in one run
-  if (T != 256 || G == 1 || N == 0 || schedule == DASH_SCHED_TABLE) return 1;
+  if (T != 256 || G == 1 || N == 0) return 1;
+  // a table in the per-head form writes one fp32 partial per query head
+  // (a whole-tile table leaves that buffer unused)
+  if (schedule == DASH_SCHED_TABLE) return G;
   if (schedule == DASH_SCHED_AUTO) {
     int m = 1;
     for (int s = DASH_SCHED_NAIVE; s <= DASH_SCHED_SYMMETRIC_SHIFT; ++s) {
@@ -407,7 +409,8 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (grid <= 0) return DASH_ERR_HIP;
   const int G = Hq / Hkv;
   const int base_items = tab ? tab->items : dash::items_per_group(mask, schedule, L.N);
-  const int ipg = base_items * L.parts;
+  // a table's items are its own; the closed forms repeat theirs per part
+  const int ipg = tab ? base_items : base_items * L.parts;
   if (tab && tab->grid > 0) grid = tab->grid;
   // The shift family waits on chains that come later in the dispatch order,
   // so the items of one part of a group must be able to run at once.
@@ -459,7 +462,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   bp.items_per_group = ipg;
   bp.total_items = B * Hkv * ipg;
   bp.parts = L.parts;
-  bp.Gp = G / L.parts;
+  bp.Gp = tab ? G : G / L.parts;
   bp.base_items = base_items;
   bp.dkv_part = L.parts > 1 ? (float*)(ws + L.dkvp) : nullptr;
   bp.NT = L.N * L.T;
@@ -488,6 +491,8 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   kp.NT = bp.NT;
   kp.D = D;
   kp.parts = L.parts;
+  // a table's partials exist only when its kernel marked them (per-head form)
+  kp.need_mark = tab ? 1 : 0;
   kp.scale = (float)(1.0 / __builtin_sqrt((double)D));
 
   dash::FinParams& fp = P->fp;
@@ -576,7 +581,7 @@ int dash_attn_bwd_table(const void* q, const void* k, const void* v, const void*
   const int T = dash_attn_tile_size(S, D);
   const int N = (S + T - 1) / T;
   const long long n = dash_schedule_table_tasks(mask, N, Hq / Hkv);
-  if (items < 1 || items > N || n < 0) return DASH_ERR_TABLE;
+  if (items < 1 || (long long)items > (long long)N * (Hq / Hkv) || n < 0) return DASH_ERR_TABLE;
   if (table_bytes < ((size_t)dash::table_task_words(items) + 2 * (size_t)n) * sizeof(unsigned))
     return DASH_ERR_TABLE;
   DeviceInfo* dev = nullptr;
@@ -622,7 +627,7 @@ int dash_attn_bwd_check(const void* workspace, void* stream) {
   if (!workspace) return DASH_ERR_NULL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
   // ctrl[1] error flag, [2] timed-out waits, [3] always zero, [4] not-prepared
-  // mark, [5] table-refused mark
+  // mark, [5] table-refused mark ([6]: per-head partials written)
   int flag[5] = {0, 0, 0, 0, 0};
   if (hipMemcpy(flag, (const int*)workspace + 1, sizeof(flag), hipMemcpyDeviceToHost) !=
       hipSuccess)

@@ -530,7 +530,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_main(BwdParams p) {
   bool acc_tail = false;  // the last four vector memory operations are partial-sum loads
   bool first_item = true;
   if constexpr (SCHED == SCHED_TABLE) {
-    if (!table_fits(p, NP)) {
+    if (!table_fits(p, NP, false)) {
       table_refused(p.ctrl);
       return;
     }

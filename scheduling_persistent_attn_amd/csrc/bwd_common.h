@@ -165,13 +165,20 @@ __device__ __forceinline__ int next_item(int* ctrl, int total, bool first) {
 // per-block offset address every block.
 // Whether a table schedule's header matches the launch: the shape, mask and
 // passes per task it was checked for, its item and task counts, and a grid
-// at least as wide as its widest dispatch block (the words are uniform).
-__device__ __forceinline__ bool table_fits(const BwdParams& p, int passes) {
+// at least as wide as its widest dispatch block (the words are uniform).  A
+// table in the per-head form also needs a kernel that writes per-head fp32
+// dK/dV partials (`split_ok`) and a partial buffer with a slot per head.
+__device__ __forceinline__ bool table_fits(const BwdParams& p, int passes, bool split_ok) {
   const unsigned* h = p.table;
-  return h[0] == kTableMagic && h[1] == (unsigned)p.N && h[2] == (unsigned)p.G && h[3] == (unsigned)p.mask &&
-         h[4] == (unsigned)passes && h[5] == (unsigned)p.items_per_group && h[6] <= gridDim.x &&
-         h[7] == (unsigned)p.table_tasks;
+  const bool split = (h[3] & kTableSplit) != 0;
+  return h[0] == kTableMagic && h[1] == (unsigned)p.N && h[2] == (unsigned)p.G &&
+         (h[3] & ~kTableSplit) == (unsigned)p.mask && h[4] == (unsigned)passes &&
+         h[5] == (unsigned)p.items_per_group && h[6] <= gridDim.x && h[7] == (unsigned)p.table_tasks &&
+         (!split || (split_ok && p.parts == p.G && p.dkv_part != nullptr));
 }
+
+// A table in the per-head form (its runs are one head's key/value tile).
+__device__ __forceinline__ bool table_split(const BwdParams& p) { return (p.table[3] & kTableSplit) != 0; }
 
 // A refused table: every workgroup leaves before touching any buffer, and
 // workgroup 0 raises the error flag and the table mark (vector stores).

@@ -307,11 +307,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
   bool acc_tail = false;  // the last two vector memory operations are partial-sum loads
   bool first_item = true;
   if constexpr (SCHED == SCHED_TABLE) {
-    if (!table_fits(p, NP)) {
+    if (!table_fits(p, NP, true)) {
       table_refused(p.ctrl);
       return;
     }
   }
+  // a table in the per-head form: each run's dK/dV go out as its head's fp32
+  // partial, summed by bwd_dkv_finalize, which looks for this mark
+  const bool split = SCHED == SCHED_TABLE && table_split(p);
+  if (split && blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(p.ctrl + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 8);
   for (;;) {
     __syncthreads();
@@ -490,11 +495,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
 #ifdef DASH_TASK_TRACE
       trace_end(trec);
 #endif
-      if (t.seg_end && p.parts > 1) {
+      if (t.seg_end && (SCHED == SCHED_TABLE ? split : p.parts > 1)) {
         // this part's fp32 dK/dV of key/value tile i (unscaled), summed over
         // the parts by bwd_dkv_finalize; rows past S are written too (the
         // buffer is padded to whole tiles) and never read
-        const long long prow = ((long long)(b * p.Hkv + hk) * p.parts + part) * p.NT + i * T + key_local;
+        const int slot = SCHED == SCHED_TABLE ? t.g : part;  // the run's head in a table
+        const long long prow = ((long long)(b * p.Hkv + hk) * p.parts + slot) * p.NT + i * T + key_local;
         float* const pk = p.dkv_part + prow * D;
         float* const pv = p.dkv_part + (long long)p.B * p.Hkv * p.parts * p.NT * D + prow * D;
 #pragma unroll
@@ -565,13 +571,16 @@ __global__ __launch_bounds__(256) void bwd_finalize_wide(FinParams p) {
 // dK/dV of split groups: dk[b, s, hk, :] = scale * sum over the parts of
 // their fp32 partials, added in ascending part order (a fixed order, so the
 // result is reproducible), then rounded to bf16; dv likewise without the
-// scale.  One thread per four features.
+// scale.  The parts are query-head parts of a closed-form schedule, or the
+// single heads of a per-head task table.  One thread per four features.
 __global__ __launch_bounds__(256) void bwd_dkv_finalize(DkvFinParams p) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int q4n = p.D / 4;
   const long long total = 2LL * p.B * p.Hkv * p.S * q4n;
   if (idx >= total) return;
   if (__hip_atomic_load(p.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+  // after a table run: only if that table wrote per-head partials
+  if (p.need_mark && __hip_atomic_load(p.ctrl + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
   const int q4 = (int)(idx % q4n);
   long long rest = idx / q4n;
   const int hk = (int)(rest % p.Hkv);

@@ -338,11 +338,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide64(BwdParams p) {
   bool acc_tail = false;  // the last two vector memory operations are partial-sum loads
   bool first_item = true;
   if constexpr (SCHED == SCHED_TABLE) {
-    if (!table_fits(p, NP)) {
+    if (!table_fits(p, NP, true)) {
       table_refused(p.ctrl);
       return;
     }
   }
+  // a table in the per-head form: each run's dK/dV go out as its head's fp32
+  // partial, summed by bwd_dkv_finalize, which looks for this mark
+  const bool split = SCHED == SCHED_TABLE && table_split(p);
+  if (split && blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(p.ctrl + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 8);
   for (;;) {
     __syncthreads();
@@ -532,11 +537,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide64(BwdParams p) {
 #ifdef DASH_TASK_TRACE
       trace_end(trec);
 #endif
-      if (t.seg_end && p.parts > 1) {
+      if (t.seg_end && (SCHED == SCHED_TABLE ? split : p.parts > 1)) {
         // this part's fp32 dK/dV of key/value tile i (unscaled), summed over
         // the parts by bwd_dkv_finalize; rows past S are written too (the
         // buffer is padded to whole tiles) and never read
-        const long long prow = ((long long)(b * p.Hkv + hk) * p.parts + part) * p.NT + i * T + key_local;
+        const int slot = SCHED == SCHED_TABLE ? t.g : part;  // the run's head in a table
+        const long long prow = ((long long)(b * p.Hkv + hk) * p.parts + slot) * p.NT + i * T + key_local;
         float* const pk = p.dkv_part + prow * D;
         float* const pv = p.dkv_part + (long long)p.B * p.Hkv * p.parts * p.NT * D + prow * D;
 #pragma unroll

@@ -91,6 +91,8 @@ struct DkvFinParams {
   void* dv;
   const int* ctrl;        // the error flag ctrl[1] up: write nothing
   int B, Hkv, S, NT, D, parts;
+  int need_mark;          // write only if control word 6 is set (a table run
+                          // marks it when its per-head partials are written)
   float scale;            // dK = scale * sum over the parts
 };
 

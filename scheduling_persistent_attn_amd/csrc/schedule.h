@@ -133,15 +133,18 @@ DASH_HD Task task_at(int mask, int schedule, int N, int G, int item, int step) {
 
 // Packed device form of a task table (one group's items; every group runs
 // the same table).  Words: a header of kTableHeaderWords -- magic, N, G,
-// mask, passes per task, items, widest dispatch block, tasks -- then the
-// item offsets (items + 1 words, padded to an even count), then two words per
-// task: i | j << 16 and g | rank << 16 | run start << 30 | run end << 31,
-// where a run is a key/value tile's unbroken stretch of tasks in its item.
+// mask (| kTableSplit for the per-head form), passes per task, items, widest
+// dispatch block, tasks -- then the item offsets (items + 1 words, padded to
+// an even count), then two words per task: i | j << 16 and
+// g | rank << 16 | run start << 30 | run end << 31, where a run is a
+// key/value tile's unbroken stretch of tasks in its item (in the per-head
+// form, one head's: its dK/dV leave the unit as that head's fp32 partial).
 // The kernels compare the header with their launch and refuse a table made
 // for another shape or kernel, or a launch with fewer workgroups than the
 // table's widest dispatch block.
 constexpr int kTableHeaderWords = 8;
 constexpr unsigned kTableMagic = 0x54485344u;  // "DSHT"
+constexpr unsigned kTableSplit = 0x100u;       // header word 3: per-head runs
 
 // Word index of the first task, after the header and the item offsets.
 DASH_HD int table_task_words(int items) { return kTableHeaderWords + ((items + 2) & ~1); }

@@ -69,8 +69,9 @@ int table_validate(int mask, int N, int G, int items, const int* offs, const int
   if (N < 1 || N >= (1 << 14) || G < 1 || G >= (1 << 16)) return DASH_ERR_SHAPE;
   const long long n = (long long)G * table_tiles(mask, N);
   if (n > kMaxTableTasks) return DASH_ERR_UNSUPPORTED;
-  // every item holds at least one key/value tile's run
-  if (items < 1 || items > N) return DASH_ERR_TABLE;
+  // every item holds at least one run (of a key/value tile, or in the
+  // per-head form of one head's key/value tile)
+  if (items < 1 || (long long)items > (long long)G * N) return DASH_ERR_TABLE;
   if (offs[0] != 0 || offs[items] != n) return DASH_ERR_TABLE;
   for (int k = 0; k < items; ++k)
     if (offs[k + 1] <= offs[k]) return DASH_ERR_TABLE;
@@ -88,31 +89,45 @@ int table_validate(int mask, int N, int G, int items, const int* offs, const int
     rank_seen[b + r] = 1;
     kv_seen[b + i] = 1;
   }
-  // one contiguous run per key/value tile (all its heads and query tiles)
-  std::vector<int> run_item(N, -1);
-  for (int k = 0; k < items; ++k) {
-    int prev = -1;
-    for (int t = offs[k]; t < offs[k + 1]; ++t) {
-      const int i = tasks[4 * t + 1];
-      if (i == prev) continue;
-      if (run_item[i] != -1) return DASH_ERR_TABLE;
-      run_item[i] = k;
-      prev = i;
+  // runs: one contiguous run per key/value tile (all its heads and query
+  // tiles), or else one per (head, key/value tile)
+  bool tile_form = true, head_form = true;
+  {
+    std::vector<char> tile_run(N, 0), head_run((size_t)G * N, 0);
+    for (int k = 0; k < items; ++k) {
+      int prev_i = -1, prev_gi = -1;
+      for (int t = offs[k]; t < offs[k + 1]; ++t) {
+        const int g = tasks[4 * t], i = tasks[4 * t + 1], gi = g * N + i;
+        if (i != prev_i) {
+          if (tile_run[i]) tile_form = false;
+          tile_run[i] = 1;
+          prev_i = i;
+        }
+        if (gi != prev_gi) {
+          if (head_run[gi]) head_form = false;
+          head_run[gi] = 1;
+          prev_gi = gi;
+        }
+      }
     }
   }
+  if (!tile_form && !head_form) return DASH_ERR_TABLE;
+  const bool split = !tile_form;
   if (out) {
     out->offs.assign(offs, offs + items + 1);
     out->tasks.resize((size_t)n);
     for (long long t = 0; t < n; ++t)
       out->tasks[t] = {tasks[4 * t], tasks[4 * t + 1], tasks[4 * t + 2], tasks[4 * t + 3]};
+    out->split = split;
   }
   if (packed) {
     packed->resize((size_t)n * 2);
+    auto run_key = [&](long long t) { return split ? tasks[4 * t] * N + tasks[4 * t + 1] : tasks[4 * t + 1]; };
     for (int k = 0; k < items; ++k) {
       for (int t = offs[k]; t < offs[k + 1]; ++t) {
         const int i = tasks[4 * t + 1];
-        const uint32_t begin = t == offs[k] || tasks[4 * (t - 1) + 1] != i;
-        const uint32_t end = t == offs[k + 1] - 1 || tasks[4 * (t + 1) + 1] != i;
+        const uint32_t begin = t == offs[k] || run_key(t - 1) != run_key(t);
+        const uint32_t end = t == offs[k + 1] - 1 || run_key(t + 1) != run_key(t);
         (*packed)[2 * t] = (uint32_t)i | ((uint32_t)tasks[4 * t + 2] << 16);
         (*packed)[2 * t + 1] =
             (uint32_t)tasks[4 * t] | ((uint32_t)tasks[4 * t + 3] << 16) | (begin << 30) | (end << 31);
@@ -190,7 +205,7 @@ int table_protocol(int mask, int N, const GroupTable& tb, int passes, int P, int
     int t0 = tb.offs[k];
     while (t0 < tb.offs[k + 1]) {
       int t1 = t0;
-      while (t1 + 1 < tb.offs[k + 1] && tb.tasks[t1 + 1].i == tb.tasks[t0].i) ++t1;
+      while (t1 + 1 < tb.offs[k + 1] && same_run(tb, (size_t)t1)) ++t1;
       // passes 0 .. L of the run; pass m takes the turn of m-1 at its end
       // and publishes m-3 in its body; the drain publishes the rest
       const long long L = (long long)(t1 - t0 + 1) * passes - 1;
@@ -298,10 +313,96 @@ bool family_applies(int mask, int N, int kind) {
   switch (kind) {
     case DASH_FAMILY_SYMMETRIC: return mask == MASK_CAUSAL && N % 2 == 0;
     case DASH_FAMILY_SHIFT:
-    case DASH_FAMILY_DESCENDING: return true;
+    case DASH_FAMILY_DESCENDING:
+    case DASH_FAMILY_PACKED: return true;
     case DASH_FAMILY_ASCENDING: return mask == MASK_FULL;  // causal: the shift walk
     default: return false;
   }
+}
+
+namespace {
+
+// The packed family: every (head, key/value tile) chain on its own -- the
+// shift walk of that tile (causal: the diagonal upward; full: cyclic from
+// the diagonal) -- packed longest first into `bins` items, each chain to the
+// least loaded bin (lower index on ties); non-empty bins in index order are
+// the items.  A task's no-wait start is its position in its item (the items
+// start together, one per workgroup), and dQ tile (g, j) is reduced in the
+// order (position, item).  Every wait then points to an earlier position,
+// or to the same position in an earlier item, so the order has no cycle.
+// With grouped heads the chains of one key/value tile land in different
+// items: the per-head form.
+GroupTable packed_table(int mask, int N, int G, int bins) {
+  struct Chain {
+    int len, g, i;
+  };
+  std::vector<Chain> chains;
+  chains.reserve((size_t)G * N);
+  for (int g = 0; g < G; ++g)
+    for (int i = 0; i < N; ++i) chains.push_back({mask == MASK_CAUSAL ? N - i : N, g, i});
+  std::stable_sort(chains.begin(), chains.end(), [](const Chain& a, const Chain& b) {
+    return a.len != b.len ? a.len > b.len : (a.g != b.g ? a.g < b.g : a.i < b.i);
+  });
+  std::vector<long long> load(bins, 0);
+  std::vector<std::vector<int>> bin_chains(bins);
+  for (int c = 0; c < (int)chains.size(); ++c) {
+    int b = 0;
+    for (int x = 1; x < bins; ++x)
+      if (load[x] < load[b]) b = x;
+    bin_chains[b].push_back(c);
+    load[b] += chains[c].len;
+  }
+  GroupTable tb;
+  tb.offs.push_back(0);
+  std::vector<int> pos;  // position of each task in its item
+  for (int b = 0; b < bins; ++b) {
+    if (bin_chains[b].empty()) continue;
+    int at = 0;
+    for (int c : bin_chains[b]) {
+      const Chain& ch = chains[c];
+      for (int s = 0; s < ch.len; ++s) {
+        const int j = mask == MASK_CAUSAL ? ch.i + s : (ch.i + s) % N;
+        tb.tasks.push_back({ch.g, ch.i, j, 0});
+        pos.push_back(at++);
+      }
+    }
+    tb.offs.push_back((int)tb.tasks.size());
+  }
+  // the form: whole-tile when each key/value tile's chains happen to form
+  // one run (always with one head), else per-head
+  {
+    std::vector<char> seen(N, 0);
+    bool tile_form = true;
+    for (size_t k = 0; k + 1 < tb.offs.size() && tile_form; ++k)
+      for (int t = tb.offs[k]; t < tb.offs[k + 1]; ++t)
+        if (t == tb.offs[k] || tb.tasks[t].i != tb.tasks[t - 1].i) {
+          if (seen[tb.tasks[t].i]) {
+            tile_form = false;
+            break;
+          }
+          seen[tb.tasks[t].i] = 1;
+        }
+    tb.split = !tile_form;
+  }
+  // ranks: (position, item) order per dQ tile
+  const int items = (int)tb.offs.size() - 1;
+  std::vector<std::vector<std::tuple<int, int, int>>> at((size_t)G * N);
+  for (int k = 0; k < items; ++k)
+    for (int t = tb.offs[k]; t < tb.offs[k + 1]; ++t)
+      at[(size_t)tb.tasks[t].g * N + tb.tasks[t].j].push_back({pos[t], k, t});
+  for (auto& v : at) {
+    std::sort(v.begin(), v.end());
+    for (int r = 0; r < (int)v.size(); ++r) tb.tasks[std::get<2>(v[r])].rank = r;
+  }
+  return tb;
+}
+
+}  // namespace
+
+int packed_bins(int N, int G, int groups, int P) {
+  const long long chains = (long long)G * N;
+  const long long b = groups >= 1 ? P / groups : P;
+  return (int)std::max(1LL, std::min(chains, b));
 }
 
 // The family's table: units (chains, or symmetric pairs) in ascending or
@@ -311,6 +412,7 @@ bool family_applies(int mask, int N, int kind) {
 // at which the unit reaches j, unit position) -- lockstep arrival inside a
 // block, blocks one after another.
 GroupTable family_table(int mask, int N, int G, int kind, int order, int block) {
+  if (kind == DASH_FAMILY_PACKED) return packed_table(mask, N, G, std::max(1, block));
   const int units = kind == DASH_FAMILY_SYMMETRIC ? N / 2 : N;
   std::vector<std::vector<std::pair<int, int>>> walks(units);
   std::vector<int> unit_of(units);
@@ -383,6 +485,17 @@ int dash_schedule_table_closed_form(int mask, int schedule, int N, int G, int* i
   return DASH_OK;
 }
 
+int dash_schedule_table_family(int mask, int N, int G, int kind, int order, int block, int* items,
+                               int* item_offsets, int* tasks) {
+  if (!items || !item_offsets || !tasks) return DASH_ERR_NULL;
+  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return DASH_ERR_SCHEDULE_MASK;
+  if (N < 1 || G < 1 || block < 1 || (order != 0 && order != 1)) return DASH_ERR_SHAPE;
+  if (!dash::family_applies(mask, N, kind)) return DASH_ERR_SCHEDULE_MASK;
+  if ((long long)G * dash::table_tiles(mask, N) > dash::kMaxTableTasks) return DASH_ERR_UNSUPPORTED;
+  write_table(dash::family_table(mask, N, G, kind, order, block), items, item_offsets, tasks);
+  return DASH_OK;
+}
+
 int dash_schedule_table_check(int S, int D, int mask, int G, int P, int items, const int* item_offsets,
                               const int* tasks) {
   const int T = dash_attn_tile_size(S, D);
@@ -392,6 +505,8 @@ int dash_schedule_table_check(int S, int D, int mask, int G, int P, int items, c
   dash::GroupTable tb;
   int st = dash::table_validate(mask, N, G, items, item_offsets, tasks, &tb, nullptr);
   if (st != DASH_OK) return st;
+  // per-head runs need the 256-key tile kernels' fp32 partial dK/dV
+  if (tb.split && T != 256) return DASH_ERR_UNSUPPORTED;
   return dash::table_protocol(mask, N, tb, dash::passes_per_task(T, D), P, nullptr, nullptr);
 }
 
@@ -412,6 +527,7 @@ size_t dash_schedule_table_pack(int S, int D, int mask, int G, int items, const 
   dash::GroupTable tb;
   std::vector<uint32_t> words;
   int st = dash::table_validate(mask, N, G, items, item_offsets, tasks, &tb, &words);
+  if (st == DASH_OK && tb.split && T != 256) st = DASH_ERR_UNSUPPORTED;
   int widest = 0;
   const int passes = dash::passes_per_task(T, D);
   // any grid at least as wide as the widest block: checked by the kernels
@@ -429,7 +545,8 @@ size_t dash_schedule_table_pack(int S, int D, int mask, int G, int items, const 
     return bytes;
   }
   uint32_t* w = (uint32_t*)out;
-  const uint32_t hdr[dash::kTableHeaderWords] = {dash::kTableMagic, (uint32_t)N, (uint32_t)G, (uint32_t)mask,
+  const uint32_t form = tb.split ? dash::kTableSplit : 0u;
+  const uint32_t hdr[dash::kTableHeaderWords] = {dash::kTableMagic, (uint32_t)N, (uint32_t)G, (uint32_t)mask | form,
                                                  (uint32_t)passes, (uint32_t)items, (uint32_t)widest,
                                                  (uint32_t)n};
   for (int x = 0; x < dash::kTableHeaderWords; ++x) w[x] = hdr[x];
@@ -462,17 +579,22 @@ int dash_schedule_search(int S, int D, int mask, int G, int groups, int P, doubl
   const int N = (S + T - 1) / T;
   if ((long long)G * dash::table_tiles(mask, N) > dash::kMaxTableTasks) return DASH_ERR_UNSUPPORTED;
   const int passes = dash::passes_per_task(T, D);
-  static const int kinds[4] = {DASH_FAMILY_SYMMETRIC, DASH_FAMILY_SHIFT, DASH_FAMILY_DESCENDING,
-                               DASH_FAMILY_ASCENDING};
+  static const int kinds[5] = {DASH_FAMILY_SYMMETRIC, DASH_FAMILY_SHIFT, DASH_FAMILY_DESCENDING,
+                               DASH_FAMILY_ASCENDING, DASH_FAMILY_PACKED};
   bool found = false;
   dash::GroupTable best;
   dash_sim_result best_res = {};
   int best_fam[3] = {0, 0, 0};
   for (int kind : kinds) {
     if (!dash::family_applies(mask, N, kind)) continue;
+    // per-head tables run on the 256-key tile kernels only
+    if (kind == DASH_FAMILY_PACKED && G > 1 && T != 256) continue;
+    const bool packed = kind == DASH_FAMILY_PACKED;
     const int units = kind == DASH_FAMILY_SYMMETRIC ? N / 2 : N;
-    for (int order = 0; order < 2; ++order) {
-      for (int b : dash::family_blocks(units, P)) {
+    const std::vector<int> blocks =
+        packed ? std::vector<int>{dash::packed_bins(N, G, groups, P)} : dash::family_blocks(units, P);
+    for (int order = 0; order < (packed ? 1 : 2); ++order) {
+      for (int b : blocks) {
         dash::GroupTable tb = dash::family_table(mask, N, G, kind, order, b);
         int st = dash::table_protocol(mask, N, tb, passes, P, nullptr, nullptr);
         if (st == DASH_ERR_TABLE) continue;

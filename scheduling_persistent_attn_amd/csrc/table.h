@@ -20,18 +20,31 @@ struct TableTask {
   int g, i, j, rank;
 };
 
-// One group's items: item k is tasks[offs[k] .. offs[k+1]).
+// One group's items: item k is tasks[offs[k] .. offs[k+1]).  A run is an
+// unbroken stretch of one key/value tile's tasks in an item (the unit keeps
+// that tile's dK/dV in registers): in the whole-tile form one run per
+// key/value tile holds all its heads; in the per-head form (split) one run
+// per (query head, key/value tile), whose dK/dV leave the unit as that head's
+// fp32 partial.
 struct GroupTable {
   std::vector<int> offs;
   std::vector<TableTask> tasks;
+  bool split = false;
 };
+
+// Whether task t + 1 continues task t's run.
+inline bool same_run(const GroupTable& tb, size_t t) {
+  return tb.tasks[t + 1].i == tb.tasks[t].i && (!tb.split || tb.tasks[t + 1].g == tb.tasks[t].g);
+}
 
 // Tiles of one query head (full: N*N, causal: N(N+1)/2).
 long long table_tiles(int mask, int N);
 
 // Structural checks of a table (every tile of every head exactly once, the
-// ranks of each dQ tile a permutation, each key/value tile's tasks one
-// contiguous run inside one item); on success fills *out and, if `packed` is
+// ranks of each dQ tile a permutation, and either each key/value tile's tasks
+// one contiguous run inside one item -- the whole-tile form, preferred when
+// both hold -- or each (head, key/value tile)'s tasks one such run -- the
+// per-head form); on success fills *out (with its form) and, if `packed` is
 // given, the device form: two words per task, i | j << 16 and
 // g | rank << 16 | run start << 30 | run end << 31.
 int table_validate(int mask, int N, int G, int items, const int* offs, const int* tasks, GroupTable* out,
@@ -53,9 +66,14 @@ GroupTable closed_form_table(int mask, int schedule, int N, int G);
 // Passes per task of the kernel for tiles of T keys at head dim D.
 int passes_per_task(int T, int D);
 
-// The searched family (see table.cpp).
+// The searched family (see table.cpp).  For DASH_FAMILY_PACKED `block` is
+// the number of bins.
 bool family_applies(int mask, int N, int kind);
 GroupTable family_table(int mask, int N, int G, int kind, int order, int block);
 std::vector<int> family_blocks(int units, int P);
+
+// Bins of the packed family for `groups` groups on P workgroups: the
+// workgroups one group gets, at most the G * N chains.
+int packed_bins(int N, int G, int groups, int P);
 
 }  // namespace dash

@@ -7,6 +7,10 @@
   element by element, to the parity bar of tests/gpu_util.py, with every turn
   counter ending at its contributor count.
 * 20 perturbed runs of a searched table are bitwise identical.
+* Packed tables in the per-head form (each run one query head's key/value
+  tile, dK/dV summed over fp32 per-head partials) against the float64
+  oracle, with counters, a bitwise rerun, and a whole-tile table run next on
+  the same workspace (the per-head mark does not outlive its run).
 * The kernel refuses a table made for another kernel, and a launch narrower
   than the table's widest dispatch block: nothing is written and
   dash_attn_bwd_check reports DASH_ERR_TABLE (the kernels return before any
@@ -151,6 +155,63 @@ def test_searched_table_bit_identical_over_runs():
             first = cur
         for a, b in zip(first, cur):
             assert np.array_equal(a, b), n
+
+
+PACKED = [
+    # B, S, Hq, Hkv, D, causal, grid
+    (1, 2048, 8, 2, 128, True, 16),   # T = 256, N = 8, G = 4: 32 walks per group into 8 items
+    (2, 1900, 6, 2, 64, True, 12),    # D = 64, ragged last tile, G = 3
+    (1, 2048, 4, 1, 128, False, 6),   # full mask, G = 4 on 6 workgroups
+    (1, 3000, 7, 1, 128, True, 20),   # seven heads per group, ragged, N = 12
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=lambda c: "B%dS%dH%d-%dD%d%s-P%d" % (
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "f", c[6]))
+def test_packed_per_head_table_parity(case):
+    from oracle import search as se
+    B, S, Hq, Hkv, D, causal, grid = case
+    T, N = _tiles(S, D)
+    assert T == 256
+    G = Hq // Hkv
+    bins = se.packed_bins(N, G, B * Hkv, grid)
+    offs, tasks = dash.dash_schedule_table_family(int(causal), N, G, dash.FAMILY_PACKED, 0, bins)
+    tl = [tuple(int(v) for v in t) for t in np.asarray(tasks).tolist()]
+    assert se.table_form([int(v) for v in offs], tl) == "head"
+    assert dash.dash_schedule_table_check(S, D, int(causal), G, grid, offs, tasks) == dash.DASH_OK
+    print("packed per-head table", case, "items", len(offs) - 1, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=5500)
+    h = {k: gu.host64(v) for k, v in x.items()}
+    dq_ref, dk_ref, dv_ref = oa.attention_backward(h["q"], h["k"], h["v"], h["do"], causal)
+    o, lse = gu.run_forward(x, causal)
+    table, items = dash.upload_table(x["q"], x["k"], causal, offs, tasks)
+    ws = dash.new_workspace(x["q"], x["k"], int(causal), dash.TABLE)
+    out = dash.backward_table(x["q"], x["k"], x["v"], o, x["do"], lse, causal, table, items,
+                              grid=grid, workspace=ws)
+    for name, got, ref in zip(("dq", "dk", "dv"), out, (dq_ref, dk_ref, dv_ref)):
+        e = gu.errors(gu.host64(got), ref)
+        print("  %s rel-l2 %.3e max-abs(excess) %.3e max-abs %.3e" % ((name,) + e))
+        assert gu.within(e), (name, e)
+    cnt = gu.read_counters(ws, B, Hq, S, D)
+    assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
+    again = dash.backward_table(x["q"], x["k"], x["v"], o, x["do"], lse, causal, table, items,
+                                grid=grid, workspace=ws)
+    for a, b in zip(out, again):
+        assert _same(a, b)
+    # a whole-tile table next on the same workspace, on other inputs: its
+    # kernel writes dK/dV itself, and the partial sum of the stale per-head
+    # partials must not overwrite them (a fresh workspace gives the reference)
+    print("  whole-tile table after it", flush=True)
+    x2 = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=5501)
+    o2, lse2 = gu.run_forward(x2, causal)
+    offs2, tasks2 = dash.dash_schedule_table_closed_form(int(causal), dash.NAIVE, N, G)
+    table2, items2 = dash.upload_table(x2["q"], x2["k"], causal, offs2, tasks2)
+    got2 = dash.backward_table(x2["q"], x2["k"], x2["v"], o2, x2["do"], lse2, causal, table2,
+                               items2, workspace=ws)
+    ref2 = dash.backward_table(x2["q"], x2["k"], x2["v"], o2, x2["do"], lse2, causal, table2,
+                               items2)
+    for a, b in zip(got2, ref2):
+        assert _same(a, b)
 
 
 def _sentinel_outputs(x):

@@ -21,12 +21,15 @@ import pytest
 from oracle import schedule as sch
 
 
-def program(tasks, ranks, NP, release_before_wait=True):
+def program(tasks, ranks, NP, release_before_wait=True, split=False):
+    # split: runs end where the head or the KV tile changes (per-head tables),
+    # else only where the KV tile changes
     ops = []
     prev = fin = rel = None
+    key = (lambda t: (t[0], t[1])) if split else (lambda t: t[1])
     for k, (g, i, j) in enumerate(tasks):
-        seg_begin = k == 0 or tasks[k - 1][1] != i
-        seg_end = k == len(tasks) - 1 or tasks[k + 1][1] != i
+        seg_begin = k == 0 or key(tasks[k - 1]) != key(tasks[k])
+        seg_end = k == len(tasks) - 1 or key(tasks[k + 1]) != key(tasks[k])
         if seg_begin:
             prev = fin = None
         for hp in range(NP):

@@ -154,9 +154,10 @@ def _all_tables(mask, N):
                     yield offs, tasks
 
 
-def _programs(offs, tasks, passes):
+def _programs(offs, tasks, passes, split=False):
     ranks = {(g, i, j): r for (g, i, j, r) in tasks}
-    return [program([(g, i, j) for (g, i, j, _) in tasks[offs[k]:offs[k + 1]]], ranks, passes)
+    return [program([(g, i, j) for (g, i, j, _) in tasks[offs[k]:offs[k + 1]]], ranks, passes,
+                    split=split)
             for k in range(len(offs) - 1)]
 
 
@@ -277,3 +278,128 @@ def test_search_reaches_more_chains_than_workers():
     assert rep["makespan"] == pytest.approx(N * N / P * 1.25)
     co, ct = se.closed_form_table(sch.SHIFT, sch.FULL, N)
     assert not se.protocol_ok(sch.FULL, N, co, ct, 8, P)[0]
+
+
+# ---- per-head tables and the packed kind -------------------------------------
+
+def _head_tables(mask, N, G, rng, n):
+    """Seeded random tables whose runs are (head, KV tile) pairs: shuffled
+    walks, ranks and run order, random item cuts."""
+    out = []
+    for _ in range(n):
+        chains = []
+        for g in range(G):
+            for i in range(N):
+                js = [j for j in range(N) if sch.valid(mask, i, j)]
+                rng.shuffle(js)
+                chains.append([(g, i, j) for j in js])
+        rng.shuffle(chains)
+        rank = {}
+        for g in range(G):
+            for j in range(N):
+                cs = list(sch.contributors(mask, N, j))
+                rng.shuffle(cs)
+                for r, i in enumerate(cs):
+                    rank[(g, i, j)] = r
+        offs, tasks = [0], []
+        for x, ch in enumerate(chains):
+            tasks.extend(t + (rank[t],) for t in ch)
+            if x == len(chains) - 1 or rng.random() < 0.4:
+                offs.append(len(tasks))
+        out.append((offs, tasks))
+    return out
+
+
+@pytest.mark.parametrize("mask,N", [(sch.FULL, 2), (sch.CAUSAL, 3), (sch.FULL, 3)])
+@pytest.mark.parametrize("passes", [1, 2, 3])
+def test_event_graph_matches_the_replayed_program_per_head(mask, N, passes):
+    # per-head runs: the check's waits-for graph agrees with the replayed
+    # hand-off programs whose runs end where the head or the tile changes
+    import random
+    rng = random.Random(1000 * N + passes)
+    tables = _head_tables(mask, N, 2, rng, 300) + [se.packed_table(mask, N, 2, b) for b in (2, 3, 4)]
+    heads = agree = 0
+    for offs, tasks in tables:
+        assert se.structure_ok(mask, N, 2, offs, tasks)
+        split = se.table_form(offs, tasks) == "head"
+        heads += split
+        done = _complete_alone(_programs(offs, tasks, passes, split))
+        assert se.events_acyclic(offs, tasks, passes, split) == done
+        agree += done
+    assert heads > 0 and 0 < agree < len(tables)
+
+
+def test_check_is_sound_on_fewer_workers_per_head():
+    import random
+    rng = random.Random(7)
+    passes, P, accepted = 2, 2, 0
+    for offs, tasks in _head_tables(sch.FULL, 2, 2, rng, 200):
+        if se.table_form(offs, tasks) != "head" or len(offs) - 1 <= P:
+            continue
+        if not se.protocol_ok(sch.FULL, 2, offs, tasks, passes, P)[0]:
+            continue
+        accepted += 1
+        assert not _deadlock_reachable(_programs(offs, tasks, passes, True), P)
+    assert accepted > 0
+
+
+def test_a_split_head_run_is_neither_form():
+    # head 0 of KV tile 0 in two pieces: not one run per tile, nor per head
+    offs = [0, 1, 3, 4]
+    tasks = [(0, 0, 0, 0), (0, 1, 0, 1), (0, 1, 1, 0), (0, 0, 1, 1)]
+    assert se.table_form(offs, tasks) is None
+    assert not se.structure_ok(sch.FULL, 2, 1, offs, tasks)
+
+
+PACKED_CASES = [(m, N, G, b) for m in (sch.FULL, sch.CAUSAL)
+                for (N, G, b) in ((1, 1, 1), (2, 3, 4), (4, 2, 3), (5, 3, 4), (8, 4, 6), (3, 2, 100),
+                                  (16, 7, 16))]
+
+
+@pytest.mark.parametrize("mask,N,G,bins", PACKED_CASES)
+def test_packed_table(mask, N, G, bins):
+    offs, tasks = se.packed_table(mask, N, G, bins)
+    assert se.structure_ok(mask, N, G, offs, tasks)
+    items = len(offs) - 1
+    assert items == min(bins, G * N)
+    # each (head, KV tile) is one run that walks its Q tiles from the
+    # diagonal on, wrapping round under the full mask
+    for k in range(items):
+        chunk = tasks[offs[k]:offs[k + 1]]
+        x = 0
+        while x < len(chunk):
+            g, i = chunk[x][0], chunk[x][1]
+            js = [j for (gg, ii, j, _) in chunk if (gg, ii) == (g, i)]
+            want = [(i + s) % N for s in range(N)] if mask == sch.FULL else list(range(i, N))
+            assert js == want
+            assert chunk[x:x + len(js)] == [t for t in chunk if (t[0], t[1]) == (g, i)]
+            x += len(js)
+    # greedy placement: the fullest item holds at most the mean of the rest
+    # plus the longest walk
+    loads = [offs[k + 1] - offs[k] for k in range(items)]
+    longest = N
+    total = len(tasks)
+    assert max(loads) <= (total - longest) / items + longest
+    # all items resident, equal task costs and no reduction cost: no wait
+    # is exposed, every item ends at its own length
+    rep = se.simulate_table(mask, N, G, 1, items, offs, tasks, 1.0, 1.0, 0.0)
+    assert not rep["deadlock"]
+    assert rep["makespan"] == max(loads)
+    split = se.table_form(offs, tasks) == "head"
+    for passes in (2, 4, 8):      # the kernels run 2 to 8 passes per task
+        assert se.protocol_ok(mask, N, offs, tasks, passes, items)[0]
+    if N <= 5:
+        assert _complete_alone(_programs(offs, tasks, 2, split))
+
+
+def test_search_packs_grouped_heads():
+    # causal, seven heads per group: the packed kind spreads the G * N walks
+    # over the grid share of each group and wins; kept out when per-head
+    # tables cannot run
+    m, N, G, groups, P = sch.CAUSAL, 8, 7, 2, 16
+    offs, tasks, fam, rep = se.search(m, N, G, groups, P, 8, 1.0, 0.5, 0.125)
+    assert fam == (se.PACKED, 0, se.packed_bins(N, G, groups, P))
+    assert se.table_form(offs, tasks) == "head"
+    offs2, tasks2, fam2, rep2 = se.search(m, N, G, groups, P, 8, 1.0, 0.5, 0.125, head_form_ok=False)
+    assert fam2[0] != se.PACKED
+    assert rep["makespan"] < rep2["makespan"]

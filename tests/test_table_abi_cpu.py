@@ -143,7 +143,8 @@ def test_search_equals_oracle(S, D, m, G, groups, P):
     N, passes = SHAPES[(S, D)]
     c, cd, r = 1.0, 0.5, 0.125
     got = dash.dash_schedule_search(S, D, m, G, groups, P, c, cd, r)
-    offs, tasks, fam, rep = se.search(m, N, G, groups, P, passes, c, cd, r)
+    head_form_ok = dash.dash_attn_tile_size(S, D) == 256
+    offs, tasks, fam, rep = se.search(m, N, G, groups, P, passes, c, cd, r, head_form_ok)
     assert _lists(got["item_offsets"], got["tasks"]) == (offs, tasks)
     assert got["family"] == fam
     assert got["report"]["makespan"] == rep["makespan"]
@@ -213,7 +214,7 @@ def test_bwd_table_validation_before_device():
     assert _bwd_table(table=None) == dash.DASH_ERR_NULL
     assert _bwd_table(table=(1 << 12) + 2) == dash.DASH_ERR_SHAPE
     assert _bwd_table(items=0) == dash.DASH_ERR_TABLE
-    assert _bwd_table(items=5) == dash.DASH_ERR_TABLE          # more items than tiles
+    assert _bwd_table(items=9) == dash.DASH_ERR_TABLE          # more items than G * N runs
     assert _bwd_table(tb=64) == dash.DASH_ERR_TABLE            # shorter than the table
     assert _bwd_table(Hq=3, Hkv=2) == dash.DASH_ERR_SHAPE
     assert _bwd_table(D=96) == dash.DASH_ERR_UNSUPPORTED
@@ -227,13 +228,108 @@ def test_bwd_table_validation_before_device():
                                         1 << 30, None) == dash.DASH_ERR_SCHEDULE_MASK
 
 
-def test_table_workspace_has_no_head_split():
-    # a table keeps a key/value tile's heads in one run: no split partials
+def test_table_workspace_holds_per_head_partials():
+    # with 256-key tiles and grouped heads a table may be in the per-head
+    # form: the workspace keeps one fp32 dK/dV partial per query head, the
+    # most any closed form splits into
     for (B, Hq, Hkv, S) in ((1, 8, 1, 4096), (2, 4, 2, 2048)):
-        assert dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, 128, 0, dash.TABLE) == 1
+        G = Hq // Hkv
+        assert dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, 128, 0, dash.TABLE) == G
         n_t = dash.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, 128, 0, dash.TABLE)
-        assert n_t > 0
         assert dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, 128, 0, dash.SHIFT) > 1
-        assert n_t < dash.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, 128, 0, dash.SHIFT)
+        assert n_t >= dash.dash_attn_bwd_workspace_size(B, Hq, Hkv, S, 128, 0, dash.SHIFT)
+    # one head per group, or small tiles: no partials
+    assert dash.dash_attn_bwd_head_parts(1, 4, 4, 4096, 128, 0, dash.TABLE) == 1
+    assert dash.dash_attn_bwd_head_parts(1, 4, 2, 512, 128, 0, dash.TABLE) == 1
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 0, dash.TABLE) == \
         dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 0, dash.NAIVE)
+
+
+FAMILY_CASES = [(m, N, G, kind, order, block)
+                for m in (sch.FULL, sch.CAUSAL)
+                for (N, G) in ((1, 1), (2, 3), (4, 2), (6, 1), (8, 3))
+                for kind in (se.SYMMETRIC, se.SHIFT, se.DESCENDING, se.ASCENDING, se.PACKED)
+                for order in ((0,) if kind == se.PACKED else (0, 1))
+                for block in (1, 2, 3, 5, 64)
+                if se.family_applies(m, N, kind) and (kind == se.PACKED or block <= max(1, N))]
+
+
+@pytest.mark.parametrize("m,N,G,kind,order,block", FAMILY_CASES)
+def test_family_tables_equal_oracle(m, N, G, kind, order, block):
+    got = _lists(*dash.dash_schedule_table_family(m, N, G, kind, order, block))
+    assert got == tuple(se.family_table(m, N, G, kind, order, block))
+
+
+def test_family_arguments():
+    with pytest.raises(ValueError):
+        dash.dash_schedule_table_family(sch.CAUSAL, 4, 2, dash.FAMILY_PACKED, 1, 4)
+    o, t = dash._table_out(8, 8)
+    items = ctypes.c_int()
+    f = dash.lib().dash_schedule_table_family
+    # symmetric pairs need the causal mask and even N; blocks start at 1
+    assert f(sch.FULL, 4, 1, dash.FAMILY_SYMMETRIC, 0, 1, ctypes.byref(items), dash._iptr(o),
+             dash._iptr(t)) != dash.DASH_OK
+    assert f(sch.CAUSAL, 4, 1, dash.FAMILY_SHIFT, 0, 0, ctypes.byref(items), dash._iptr(o),
+             dash._iptr(t)) != dash.DASH_OK
+    assert f(sch.CAUSAL, 4, 1, 9, 0, 1, ctypes.byref(items), dash._iptr(o),
+             dash._iptr(t)) != dash.DASH_OK
+
+
+def test_per_head_tables_on_256_key_tiles_only():
+    # a packed table of two heads is in the per-head form: accepted with
+    # 256-key tiles (S = 1024, D = 128 gives 4 tiles), refused with 128-key
+    # tiles (S = 512, D = 128 gives 4 tiles as well)
+    m, N, G = sch.CAUSAL, 4, 2
+    offs, tasks = dash.dash_schedule_table_family(m, N, G, dash.FAMILY_PACKED, 0, 3)
+    ol, tl = _lists(offs, tasks)
+    assert se.table_form(ol, tl) == "head"
+    assert dash.dash_attn_tile_size(1024, 128) == 256 and dash.dash_attn_tile_size(512, 128) == 128
+    assert dash.dash_schedule_table_check(1024, 128, m, G, 3, offs, tasks) == dash.DASH_OK
+    assert dash.dash_schedule_table_check(512, 128, m, G, 3, offs, tasks) == dash.DASH_ERR_UNSUPPORTED
+    with pytest.raises(dash.DashError) as e:
+        dash.dash_schedule_table_pack(512, 128, m, G, offs, tasks)
+    assert e.value.status == dash.DASH_ERR_UNSUPPORTED
+    raw = dash.dash_schedule_table_pack(1024, 128, m, G, offs, tasks)
+    w = struct.unpack("<%dI" % (len(raw) // 4), raw)
+    items, n = len(ol) - 1, len(tl)
+    assert w[3] == m | 0x100                 # the per-head form's flag beside the mask
+    assert w[5] == items and w[7] == n
+    tw = 8 + ((items + 2) & ~1)
+    for t, (g, i, j, r) in enumerate(tl):
+        w1 = w[tw + 2 * t + 1]
+        k = max(x for x in range(items) if ol[x] <= t)
+        begin = t == ol[k] or tl[t - 1][:2] != (g, i)
+        end = t == ol[k + 1] - 1 or tl[t + 1][:2] != (g, i)
+        assert ((w1 >> 30) & 1, w1 >> 31) == (begin, end)
+    # a tile-form table keeps the bare mask
+    offs2, tasks2 = dash.dash_schedule_table_closed_form(m, sch.SHIFT, N, G)
+    raw2 = dash.dash_schedule_table_pack(1024, 128, m, G, offs2, tasks2)
+    assert struct.unpack("<4I", raw2[:16])[3] == m
+
+
+def test_table_in_neither_form_is_refused():
+    # head 0 of KV tile 0 in two pieces on either side of another run
+    offs = [0, 1, 3, 4]
+    tasks = [(0, 0, 0, 0), (0, 1, 0, 1), (0, 1, 1, 0), (0, 0, 1, 1)]
+    assert dash.dash_schedule_table_check(512, 128, sch.FULL, 1, 4, offs, tasks) == dash.DASH_ERR_TABLE
+    # more items than (head, tile) runs
+    offs, tasks = dash.dash_schedule_table_family(sch.FULL, 2, 1, dash.FAMILY_PACKED, 0, 2)
+    assert len(offs) == 3
+    assert dash.dash_schedule_table_check(512, 256, sch.FULL, 1, 4, offs, tasks) in (
+        dash.DASH_OK, dash.DASH_ERR_UNSUPPORTED)
+
+
+def test_search_packs_grouped_heads():
+    # 8 tiles of 256 keys, 7 heads per group, 2 groups on 16 workgroups: the
+    # search picks the packed kind, as the oracle does
+    S, D, m, G, groups, P = 2048, 128, sch.CAUSAL, 7, 2, 16
+    c, cd, r = 1.0, 0.5, 0.125
+    got = dash.dash_schedule_search(S, D, m, G, groups, P, c, cd, r)
+    offs, tasks, fam, rep = se.search(m, 8, G, groups, P, 8, c, cd, r)
+    assert got["family"] == fam == (dash.FAMILY_PACKED, 0, se.packed_bins(8, G, groups, P))
+    assert _lists(got["item_offsets"], got["tasks"]) == (offs, tasks)
+    assert got["report"]["makespan"] == rep["makespan"]
+    # with 128-key tiles (S = 512) the per-head form cannot run
+    assert dash.dash_attn_tile_size(512, 128) == 128
+    got2 = dash.dash_schedule_search(512, 128, m, G, groups, P, c, cd, r)
+    assert got2["family"][0] != dash.FAMILY_PACKED
