@@ -16,6 +16,14 @@ last timed step's turn waits are read from the workspace: `wait_fraction` is
 the time waves spent waiting for an earlier dQ contribution, as a share of
 the persistent grid's wave time (the schedule's bubbles).
 
+The `table` row is the library's searched task table for the workload
+(dash_schedule_search over the family of walks on the device's grid, with the
+automatic selector's weights: a task costs 1, a causal diagonal task 1, the
+exposed hand-off 0.1), run as dash_attn_bwd_prepare then
+dash_attn_bwd_table_run with the same events.  When the search returns exactly
+the table of a closed form that splits no query heads it is not timed twice:
+the line names that closed form instead.
+
 The headline value is the whole-step throughput of the fastest deterministic
 schedule in TFLOP/s with FLOPs = 10*B*Hq*S^2*D (halved for a causal mask).  The
 roofline object prices the persistent backward kernel alone (events around
@@ -43,6 +51,7 @@ import hashlib
 import json
 import os
 import re
+import struct
 import sys
 import time
 
@@ -127,9 +136,47 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
+# weights of the table search: those of the library's automatic selector
+SEARCH_WEIGHTS = (1.0, 1.0, 0.1)
+
+
+def searched_table(dash, cfg):
+    """The library's searched table for the workload on the device grid:
+    {"offs", "tasks", "family", "items", "per_head", "makespan", "same_as"}."""
+    B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    mask = 1 if cfg["causal"] else 0
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    G = Hq // Hkv
+    grid = dash.dash_attn_bwd_grid_size(S, D, mask)
+    res = dash.dash_schedule_search(S, D, mask, G, B * Hkv, grid, *SEARCH_WEIGHTS)
+    offs = [int(v) for v in res["item_offsets"]]
+    tasks = [tuple(int(v) for v in t) for t in res["tasks"].tolist()]
+    raw = dash.dash_schedule_table_pack(S, D, mask, G, offs, tasks)
+    per_head = (struct.unpack_from("<I", raw, 12)[0] & 0x100) != 0
+    same_as = None
+    names = {v: k for k, v in dash.SCHEDULES.items()}
+    for s in (dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT, dash.SYMMETRIC_SHIFT):
+        if s == dash.SYMMETRIC_SHIFT and (not mask or N % 2):
+            continue
+        if dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, mask, s) != 1:
+            continue
+        co, ct = dash.dash_schedule_table_closed_form(mask, s, N, G)
+        if [int(v) for v in co] == offs and [tuple(int(v) for v in t) for t in ct.tolist()] == tasks:
+            same_as = names[s]
+            break
+    return {"offs": offs, "tasks": tasks, "family": list(res["family"]), "items": len(offs) - 1,
+            "per_head": per_head, "makespan": res["report"]["makespan"], "same_as": same_as}
+
+
+def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup, table=None):
+    """Times one schedule; `table` (from searched_table) runs the TABLE
+    schedule under that table."""
     import torch
     mask = 1 if cfg["causal"] else 0
+    if table is not None:
+        sched = dash.TABLE
+        tdev, titems = dash.upload_table(x["q"], x["k"], cfg["causal"], table["offs"], table["tasks"])
     ws = dash.new_workspace(x["q"], x["k"], mask, sched)
     dq = torch.empty_like(x["q"])
     dk = torch.empty_like(x["k"])
@@ -148,8 +195,12 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
                                    ws, s)
         if e:
             e[1].record(s)
-        dash.dash_attn_bwd_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, mask, sched,
-                               ws, s)
+        if table is not None:
+            dash.dash_attn_bwd_table_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, mask, tdev,
+                                         titems, 0, ws, s)
+        else:
+            dash.dash_attn_bwd_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, mask, sched,
+                                   ws, s)
         if e:
             e[2].record(s)
 
@@ -187,8 +238,13 @@ def time_schedule(dash, x, o, lse, cfg, sched, steps, warmup):
     st = ws[32:64].view(torch.int64).cpu().tolist()
     if st[3] > st[1] and st[2] > st[0]:
         out["sclk_mhz"] = round(100.0 * (st[2] - st[0]) / (st[3] - st[1]), 1)
-    out["head_parts"] = dash.dash_attn_bwd_head_parts(x["q"].shape[0], x["q"].shape[2], Hkv, S, D,
-                                                      mask, sched)
+    if table is not None:
+        # a per-head table writes one partial per query head; a whole-tile
+        # table none
+        out["head_parts"] = x["q"].shape[2] // Hkv if table["per_head"] else 1
+    else:
+        out["head_parts"] = dash.dash_attn_bwd_head_parts(x["q"].shape[0], x["q"].shape[2], Hkv,
+                                                          S, D, mask, sched)
     out["wait_fraction"] = wst["wait_seconds"] / (waves * kern[-1] * 1e-3)
     if warmup > 0:
         out["repro"] = reproducibility(dash, step, bits, ref, ws)
@@ -457,7 +513,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
-    ap.add_argument("--schedules", default="naive,descending_q,shift,symmetric_shift,atomic")
+    ap.add_argument("--schedules", default="naive,descending_q,shift,symmetric_shift,table,atomic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload, not the summary of the others")
@@ -540,11 +596,21 @@ def measure(dash, name, args, headline):
     fl = flops(cfg)
 
     results = {}
+    tinfo = None
     for sname in args.schedules.split(","):
-        sched = dash.SCHEDULES[sname]
-        if sched == dash.SYMMETRIC_SHIFT and (not cfg["causal"] or N % 2):
-            continue
-        r = time_schedule(dash, x, o, lse, cfg, sched, args.steps, args.warmup)
+        if sname == "table":
+            tinfo = searched_table(dash, cfg)
+            log("  searched table: family %s, %d items per group%s, simulated %.1f%s" % (
+                tinfo["family"], tinfo["items"], " (per-head form)" if tinfo["per_head"] else "",
+                tinfo["makespan"], ", same as %s" % tinfo["same_as"] if tinfo["same_as"] else ""))
+            if tinfo["same_as"]:
+                continue
+            r = time_schedule(dash, x, o, lse, cfg, None, args.steps, args.warmup, table=tinfo)
+        else:
+            sched = dash.SCHEDULES[sname]
+            if sched == dash.SYMMETRIC_SHIFT and (not cfg["causal"] or N % 2):
+                continue
+            r = time_schedule(dash, x, o, lse, cfg, sched, args.steps, args.warmup)
         r["tflops"] = fl / (r["ms_mean"] * 1e-3) / 1e12
         r["kernel_tflops"] = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
         r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
@@ -563,8 +629,11 @@ def measure(dash, name, args, headline):
     sched_out = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  for k, v in results.items()}
     mask = 1 if cfg["causal"] else 0
-    parts = dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, mask, dash.SCHEDULES[best])
+    parts = bestr["head_parts"]
     roof = roofline(cfg, T, fl, bestr["kernel_ms_mean"], best, committed_traffic(name, best), parts)
+    table_out = None
+    if tinfo is not None:
+        table_out = {k: tinfo[k] for k in ("family", "items", "per_head", "makespan", "same_as")}
     bit_identical = (all(v["repro"]["differ"] == 0 for v in det.values())
                      if all("repro" in v for v in det.values()) else None)
     names = {v: k for k, v in dash.SCHEDULES.items()}
@@ -580,7 +649,8 @@ def measure(dash, name, args, headline):
                     det_over_atomic=round(bestr["det_over_atomic"], 4) if atomic else None,
                     schedules=sched_out, roofline=roof,
                     deterministic_bit_identical=bit_identical,
-                    auto_schedule=auto, auto_is_measured_best=auto == best)
+                    auto_schedule=auto, auto_is_measured_best=auto == best,
+                    searched_table=table_out)
 
     line = {
         "metric": "deterministic attn-bwd TFLOP/s on 1 MI355X; % bf16 MFMA peak; ratio vs atomic dQ",
@@ -600,6 +670,7 @@ def measure(dash, name, args, headline):
         "det_over_atomic": round(bestr["det_over_atomic"], 4) if atomic else None,
         "schedules": sched_out,
         "roofline": roof,
+        "searched_table": table_out,
     }
     # run-to-run bit identity at this size, in this launch configuration:
     # every deterministic schedule must reproduce its first output exactly

@@ -489,6 +489,16 @@ int dash_attn_bwd_table(const void* q, const void* k, const void* v, const void*
                         size_t table_bytes, int items, int grid, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* The run phase of dash_attn_bwd_table alone, for callers that schedule or
+ * time the two phases separately: dash_attn_bwd_prepare(..., DASH_SCHED_TABLE,
+ * ...) on this workspace first, then this call (same arguments and checks as
+ * dash_attn_bwd_table less o and lse; the preparation contract of
+ * dash_attn_bwd_run, including DASH_ERR_NOT_PREPARED). */
+int dash_attn_bwd_table_run(const void* q, const void* k, const void* v, const void* dout,
+                            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D,
+                            int mask, const void* table, size_t table_bytes, int items,
+                            int grid, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ SYMBOLS = (
     "dash_schedule_table_tasks", "dash_schedule_table_closed_form", "dash_schedule_table_family",
     "dash_schedule_table_check",
     "dash_schedule_table_pack", "dash_sim_table", "dash_schedule_search", "dash_attn_bwd_table",
+    "dash_attn_bwd_table_run",
 )
 
 # bytes of the static device workspace behind dash_attn_bwd_noalloc
@@ -151,6 +152,8 @@ def _load(path):
     L.dash_schedule_search.restype = i
     L.dash_attn_bwd_table.argtypes = [p] * 9 + [i] * 6 + [p, sz, i, i, p, sz, p]
     L.dash_attn_bwd_table.restype = i
+    L.dash_attn_bwd_table_run.argtypes = [p] * 7 + [i] * 6 + [p, sz, i, i, p, sz, p]
+    L.dash_attn_bwd_table_run.restype = i
     return L
 
 
@@ -530,6 +533,31 @@ def dash_attn_bwd_table(q, k, v, o, dout, lse, dq, dk, dv, mask, table, items, g
                                    _stream(stream))
     if st != DASH_OK:
         raise DashError(st, "dash_attn_bwd_table")
+
+
+def dash_attn_bwd_table_run(q, k, v, dout, dq, dk, dv, mask, table, items, grid, workspace,
+                            stream=None):
+    """Run phase of dash_attn_bwd_table, after dash_attn_bwd_prepare with
+    the TABLE schedule on the same workspace."""
+    import torch
+    _check_tensors([("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)], torch.bfloat16)
+    _check_tensors([("table", table)], torch.uint8)
+    dims = _dims(q, k)
+    dev = _check_layout(dims, [("q", q), ("dout", dout), ("dq", dq)],
+                        [("k", k), ("v", v), ("dk", dk), ("dv", dv)])
+    _check_workspace(workspace, dev)
+    if table is not None and table.device != dev:
+        raise ValueError("table must be on the tensors' device")
+    B, S, Hq, Hkv, D = dims
+    st = lib().dash_attn_bwd_table_run(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), B, Hq, Hkv, S, D, int(mask), _ptr(table),
+                                       table.numel() if table is not None else 0, int(items),
+                                       int(grid), _ptr(workspace),
+                                       workspace.numel() if workspace is not None else 0,
+                                       _stream(stream))
+    if st != DASH_OK:
+        raise DashError(st, "dash_attn_bwd_table_run")
 
 
 def dash_attn_bwd_check(workspace, stream=None):

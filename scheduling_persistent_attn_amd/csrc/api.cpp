@@ -527,6 +527,40 @@ int launch_main_phase(const BwdPlan& P, int D, int mask, hipStream_t s) {
   return DASH_OK;
 }
 
+// dash_attn_bwd_table (phases 3: preprocess and main phase) and its run
+// phase alone (2, after dash_attn_bwd_prepare with DASH_SCHED_TABLE).
+int table_phases(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D,
+                 int mask, const void* table, size_t table_bytes, int items, int grid, void* workspace,
+                 size_t workspace_bytes, void* stream, int phases) {
+  int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_TABLE);
+  if (st != DASH_OK) return st;
+  if (B == 0 || S == 0) return DASH_OK;  // nothing to launch, as dash_attn_bwd
+  if (!table) return DASH_ERR_NULL;
+  if (!aligned(table, 4)) return DASH_ERR_SHAPE;
+  const int T = dash_attn_tile_size(S, D);
+  const int N = (S + T - 1) / T;
+  const long long n = dash_schedule_table_tasks(mask, N, Hq / Hkv);
+  if (items < 1 || (long long)items > (long long)N * (Hq / Hkv) || n < 0) return DASH_ERR_TABLE;
+  if (table_bytes < ((size_t)dash::table_task_words(items) + 2 * (size_t)n) * sizeof(unsigned))
+    return DASH_ERR_TABLE;
+  DeviceInfo* dev = nullptr;
+  st = device_info(&dev);
+  if (st != DASH_OK) return st;
+  const int full = dev->cus * blocks_per_cu(*dev, D, T, mask);
+  if (full <= 0) return DASH_ERR_HIP;
+  if (grid < 0 || grid > full) return DASH_ERR_SHAPE;
+  const TableArgs tab = {table, items, grid};
+  BwdPlan P;
+  bool empty = false;
+  st = plan_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, DASH_SCHED_TABLE, workspace,
+                workspace_bytes, phases, &P, &empty, &tab);
+  if (st != DASH_OK || empty) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((phases & 1) && dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
+  return launch_main_phase(P, D, mask, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -573,32 +607,16 @@ int dash_attn_bwd_table(const void* q, const void* k, const void* v, const void*
                         int Hq, int Hkv, int S, int D, int mask, const void* table,
                         size_t table_bytes, int items, int grid, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_TABLE);
-  if (st != DASH_OK) return st;
-  if (B == 0 || S == 0) return DASH_OK;  // nothing to launch, as dash_attn_bwd
-  if (!table) return DASH_ERR_NULL;
-  if (!aligned(table, 4)) return DASH_ERR_SHAPE;
-  const int T = dash_attn_tile_size(S, D);
-  const int N = (S + T - 1) / T;
-  const long long n = dash_schedule_table_tasks(mask, N, Hq / Hkv);
-  if (items < 1 || (long long)items > (long long)N * (Hq / Hkv) || n < 0) return DASH_ERR_TABLE;
-  if (table_bytes < ((size_t)dash::table_task_words(items) + 2 * (size_t)n) * sizeof(unsigned))
-    return DASH_ERR_TABLE;
-  DeviceInfo* dev = nullptr;
-  st = device_info(&dev);
-  if (st != DASH_OK) return st;
-  const int full = dev->cus * blocks_per_cu(*dev, D, T, mask);
-  if (full <= 0) return DASH_ERR_HIP;
-  if (grid < 0 || grid > full) return DASH_ERR_SHAPE;
-  const TableArgs tab = {table, items, grid};
-  BwdPlan P;
-  bool empty = false;
-  st = plan_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, DASH_SCHED_TABLE,
-                workspace, workspace_bytes, 3, &P, &empty, &tab);
-  if (st != DASH_OK || empty) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
-  return launch_main_phase(P, D, mask, s);
+  return table_phases(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, table, table_bytes, items,
+                      grid, workspace, workspace_bytes, stream, 3);
+}
+
+int dash_attn_bwd_table_run(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                            void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, int mask,
+                            const void* table, size_t table_bytes, int items, int grid, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return table_phases(q, k, v, nullptr, dout, nullptr, dq, dk, dv, B, Hq, Hkv, S, D, mask, table, table_bytes,
+                      items, grid, workspace, workspace_bytes, stream, 2);
 }
 
 int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,

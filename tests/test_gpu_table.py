@@ -214,6 +214,41 @@ def test_packed_per_head_table_parity(case):
         assert _same(a, b)
 
 
+def test_table_run_phase():
+    # dash_attn_bwd_prepare (TABLE) then dash_attn_bwd_table_run gives the
+    # one-call result bit for bit; a second run without a prepare computes
+    # nothing, leaves the outputs untouched (no per-head sum either) and is
+    # reported as not prepared
+    from oracle import search as se
+    B, S, Hq, Hkv, D, causal, grid = 1, 2048, 8, 2, 128, True, 16
+    T, N = _tiles(S, D)
+    G = Hq // Hkv
+    offs, tasks = dash.dash_schedule_table_family(1, N, G, dash.FAMILY_PACKED, 0,
+                                                  se.packed_bins(N, G, B * Hkv, grid))
+    print("table run phase", (B, S, Hq, Hkv, D, causal, grid), flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=5600)
+    o, lse = gu.run_forward(x, causal)
+    table, items = dash.upload_table(x["q"], x["k"], causal, offs, tasks)
+    ws = dash.new_workspace(x["q"], x["k"], 1, dash.TABLE)
+    ref = [t.clone() for t in dash.backward_table(x["q"], x["k"], x["v"], o, x["do"], lse, causal,
+                                                  table, items, grid=grid, workspace=ws)]
+    dq, dk, dv = _sentinel_outputs(x)
+    dash.dash_attn_bwd_prepare(o, x["do"], lse, tuple(x["q"].shape), Hkv, 1, dash.TABLE, ws)
+    dash.dash_attn_bwd_table_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, 1, table, items,
+                                 grid, ws)
+    dash.dash_attn_bwd_check(ws)
+    for a, b in zip(ref, (dq, dk, dv)):
+        assert _same(a, b)
+    dq, dk, dv = _sentinel_outputs(x)
+    dash.dash_attn_bwd_table_run(x["q"], x["k"], x["v"], x["do"], dq, dk, dv, 1, table, items,
+                                 grid, ws)
+    with pytest.raises(dash.DashError) as e:
+        dash.dash_attn_bwd_check(ws)
+    assert e.value.status == dash.DASH_ERR_NOT_PREPARED
+    for t in (dq, dk, dv):
+        assert torch.all(t == 7.0)
+
+
 def _sentinel_outputs(x):
     return (torch.full_like(x["q"], 7.0), torch.full_like(x["k"], 7.0), torch.full_like(x["v"], 7.0))
 
