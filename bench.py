@@ -637,6 +637,7 @@ def measure(dash, name, args, headline):
     bit_identical = (all(v["repro"]["differ"] == 0 for v in det.values())
                      if all("repro" in v for v in det.values()) else None)
     names = {v: k for k, v in dash.SCHEDULES.items()}
+    names[dash.TABLE] = "table"   # AUTO may resolve to the searched table
     auto = names[dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, 1 if cfg["causal"] else 0)]
     shape = {"B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": D,
              "mask": "causal" if cfg["causal"] else "full", "tile": T, "head_parts": parts}

@@ -66,8 +66,9 @@ enum dash_mask { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 };
  *                   (the best-balanced items; its result does not depend on
  *                   the order), one chain per KV tile otherwise; ranks are
  *                   reported in ascending KV order.
- *  AUTO             one of the four deterministic schedules, chosen per shape
- *                   and device by the schedule simulator below (see
+ *  AUTO             one of the four deterministic schedules, or the
+ *                   library's searched task table, chosen per shape and
+ *                   device by the schedule simulator below (see
  *                   dash_attn_bwd_auto_schedule); deterministic like the
  *                   schedule it resolves to.
  *  TABLE            a deterministic schedule written out task by task (a
@@ -238,7 +239,9 @@ int dash_attn_bwd_run(const void* q, const void* k, const void* v,
  * zero with kernels (no memset nodes).  Same arguments (less the workspace),
  * results, determinism contract and errors as dash_attn_bwd, plus
  * DASH_ERR_WORKSPACE, before anything is enqueued, when the problem's
- * workspace (dash_attn_bwd_workspace_size) exceeds 64 MiB.  Every call on one
+ * workspace (dash_attn_bwd_workspace_size) exceeds 64 MiB.  Here AUTO chooses
+ * among the four closed forms only (the searched table would need pinned
+ * host memory), so it may resolve differently from dash_attn_bwd's AUTO.  Every call on one
  * GPU shares that GPU's array: calls that overlap in time on one device race
  * and give undefined results; order them with a stream or events.  The
  * watchdog flag lands in the static array, where dash_attn_bwd_check cannot
@@ -281,16 +284,33 @@ int dash_attn_bwd_wait_stats(const void* workspace, size_t workspace_bytes, void
 int dash_attn_set_watchdog(double seconds);
 
 /* The deterministic schedule that DASH_SCHED_AUTO resolves to for these
- * arguments on the current device, or minus a dash_status.  The choice is
- * dash_sim_select over the device's persistent grid (P = the workgroups
- * dash_attn_bwd launches, dynamic dispatch), B*Hkv groups of Hq/Hkv query
- * heads on the tile count of (S, D), with weights c_full = c_diag = 1 (the
+ * arguments on the current device (DASH_SCHED_TABLE for the searched table),
+ * or minus a dash_status.  The closed forms are simulated over the device's
+ * persistent grid (P = the workgroups dash_attn_bwd launches, dynamic
+ * dispatch), B*Hkv groups of Hq/Hkv query heads on the tile count of (S, D),
+ * each with its own split of the query heads (a split group simulates as
+ * `parts` groups of G/parts heads), with weights c_full = c_diag = 1 (the
  * kernel computes a causal diagonal tile in full) and r = 0.1 (the exposed
  * part of a hand-off, relative to one task); SHIFT and SYMMETRIC_SHIFT are
- * candidates only when one group of items fits in the grid.  The result is
- * cached per device and shape, so a given shape on a given device always
- * runs the same schedule: AUTO keeps the determinism contract. */
+ * candidates only when one group of items fits in the grid.  The table
+ * dash_schedule_search finds with the same grid and weights is a candidate
+ * too where it needs no more workspace than the closed forms (64- or
+ * 128-key tiles, G = 1, or closed forms that already split the heads into
+ * G parts) and the problem simulates at most 2^18 tasks (B*Hkv groups times
+ * the tasks of one); it wins only with a strictly shorter critical path.
+ * The result is cached per device and shape, so a given shape on a given
+ * device always runs the same schedule: AUTO keeps the determinism
+ * contract.  When the table is chosen, its device form is kept in pinned
+ * host memory (held until the process ends) and every prepare phase copies
+ * it into the workspace, on the call's stream; the first call for a shape
+ * runs the search on the host (up to about two seconds). */
 int dash_attn_bwd_auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask);
+
+/* The same choice on the host alone, for a device whose persistent grid is
+ * `grid` workgroups (dash_attn_bwd_grid_size on that device): no device is
+ * touched and nothing is cached.  Returns the schedule or minus a
+ * dash_status (DASH_ERR_SHAPE for grid < 1 with a non-empty shape). */
+int dash_attn_bwd_auto_schedule_on(int B, int Hq, int Hkv, int S, int D, int mask, int grid);
 
 /* Static description of a status code. */
 const char* dash_status_string(int status);

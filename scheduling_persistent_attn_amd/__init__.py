@@ -39,7 +39,7 @@ SYMBOLS = (
     "dash_attn_bwd", "dash_attn_bwd_prepare", "dash_attn_bwd_run", "dash_attn_bwd_check", "dash_status_string",
     "dash_attn_bwd_grid_size", "dash_schedule_num_items",
     "dash_schedule_item_len", "dash_schedule_task", "dash_sim_run", "dash_sim_select",
-    "dash_attn_bwd_auto_schedule", "dash_attn_set_watchdog", "dash_attn_bwd_wait_stats",
+    "dash_attn_bwd_auto_schedule", "dash_attn_bwd_auto_schedule_on", "dash_attn_set_watchdog", "dash_attn_bwd_wait_stats",
     "dash_attn_bwd_noalloc", "dash_attn_bwd_head_parts",
     "dash_schedule_table_tasks", "dash_schedule_table_closed_form", "dash_schedule_table_family",
     "dash_schedule_table_check",
@@ -135,6 +135,8 @@ def _load(path):
     L.dash_sim_select.restype = i
     L.dash_attn_bwd_auto_schedule.argtypes = [i] * 6
     L.dash_attn_bwd_auto_schedule.restype = i
+    L.dash_attn_bwd_auto_schedule_on.argtypes = [i] * 7
+    L.dash_attn_bwd_auto_schedule_on.restype = i
     ip = ctypes.POINTER(ctypes.c_int)
     L.dash_schedule_table_tasks.argtypes = [i, i, i]
     L.dash_schedule_table_tasks.restype = ctypes.c_longlong
@@ -216,6 +218,15 @@ def dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, mask):
     r = lib().dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, mask)
     if r < 0:
         raise DashError(-r, "dash_attn_bwd_auto_schedule")
+    return r
+
+
+def dash_attn_bwd_auto_schedule_on(B, Hq, Hkv, S, D, mask, grid):
+    """The schedule AUTO picks for a device whose persistent grid is `grid`
+    workgroups, computed on the host alone."""
+    r = lib().dash_attn_bwd_auto_schedule_on(B, Hq, Hkv, S, D, mask, grid)
+    if r < 0:
+        raise DashError(-r, "dash_attn_bwd_auto_schedule_on")
     return r
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -73,7 +74,9 @@ int slices_per_tile(int T, int D) { return T == 256 ? T * D / 512 : T * D / 1024
 
 struct Layout {
   int T = 0, N = 0, NW = 0, parts = 1;
-  size_t ctrl = 0, waits = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, dkvp = 0, trace = 0, total = 0;
+  size_t ctrl = 0, waits = 0, counters = 0, delta = 0, lse2 = 0, dqacc = 0, dkvp = 0, table = 0, trace = 0,
+         total = 0;
+  size_t table_bytes = 0;
   long long n_counters = 0, n_rows = 0, n_dqacc = 0, n_dkvp = 0, n_trace = 0;
 };
 
@@ -156,6 +159,17 @@ int make_layout(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, La
   L->dkvp = off;
   L->n_dkvp = L->parts > 1 ? 2LL * B * Hkv * L->parts * L->N * L->T * D : 0;
   off += round256((size_t)L->n_dkvp * sizeof(float));
+  // AUTO: room for the searched table's device form, which the prepare phase
+  // copies in when AUTO resolves to it (the largest table of this shape).
+  // TABLE reserves it too, so that AUTO resolved to a table keeps every
+  // offset (the debug build's trace follows it).
+  L->table = off;
+  if (schedule == DASH_SCHED_AUTO || schedule == DASH_SCHED_TABLE) {
+    const int G = Hq / Hkv;
+    const long long n = dash_schedule_table_tasks(mask, L->N, G);
+    L->table_bytes = ((size_t)dash::table_task_words(G * L->N) + 2 * (size_t)(n > 0 ? n : 0)) * sizeof(unsigned);
+    off += round256(L->table_bytes);
+  }
 #ifdef DASH_TASK_TRACE
   // the debug build's task trace: 64 bytes per (item, step), for the
   // longest item of any schedule the call could run
@@ -169,8 +183,12 @@ int make_layout(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, La
     const long long n = items * trace_len(mask, s, L->N, Hq / Hkv / parts);
     L->n_trace = n > L->n_trace ? n : L->n_trace;
   }
-  // a table schedule: one record per task
-  if (schedule == DASH_SCHED_TABLE) L->n_trace = (long long)B * Hq * L->N * L->N;
+  // a table schedule (also the searched table AUTO may resolve to): one
+  // record per task
+  if (schedule == DASH_SCHED_TABLE || schedule == DASH_SCHED_AUTO) {
+    const long long n = (long long)B * Hq * L->N * L->N;
+    L->n_trace = n > L->n_trace ? n : L->n_trace;
+  }
   off += round256((size_t)L->n_trace * 64);
 #endif
   L->total = off;
@@ -183,14 +201,23 @@ int make_layout(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, La
 // exposed is about a tenth of a task (it is pipelined behind later passes).
 constexpr double kAutoC = 1.0, kAutoCDiag = 1.0, kAutoR = 0.1;
 
-struct AutoEntry {
-  int dev, B, Hq, Hkv, S, D, mask, schedule;
-};
-std::vector<AutoEntry> g_auto;
-std::mutex g_auto_mu;
+// AUTO considers the searched table only up to this many simulated tasks
+// (groups x tasks per group), so that its first call stays within about two
+// seconds of host time.
+constexpr long long kAutoTableSimTasks = 1LL << 18;
 
-// Resolves DASH_SCHED_AUTO for a shape on the current device (cached).
-int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
+// The choice of DASH_SCHED_AUTO on a device with `grid` persistent
+// workgroups, host only.  Every deterministic closed form that applies, each
+// with its own split of the query heads (a split group simulates as `parts`
+// groups of G/parts heads, in the same dispatch order), and with
+// `allow_table` the library's searched table (dash_schedule_search with the
+// same weights) where its workspace is the closed forms' (no head split on
+// 64/128-key tiles or with G = 1, else the closed forms already reserve G
+// partial slots).  The shortest critical path wins; ties go to the earlier
+// of SYMMETRIC_SHIFT, SHIFT, DESCENDING_Q, NAIVE, then the table.  With the
+// table chosen, `packed` receives its device form and `items` its items.
+int auto_decide(int B, int Hq, int Hkv, int S, int D, int mask, int grid, bool allow_table, int* out,
+                std::vector<unsigned char>* packed, int* items) {
   int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_NAIVE);
   if (st != DASH_OK) return st;
   Layout L;
@@ -200,30 +227,13 @@ int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
     *out = DASH_SCHED_NAIVE;
     return DASH_OK;
   }
-  DeviceInfo* dev = nullptr;
-  st = device_info(&dev);
-  if (st != DASH_OK) return st;
-  int dev_id = 0;
-  if (hipGetDevice(&dev_id) != hipSuccess) return DASH_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_auto_mu);
-  for (const AutoEntry& e : g_auto)
-    if (e.dev == dev_id && e.B == B && e.Hq == Hq && e.Hkv == Hkv && e.S == S && e.D == D &&
-        e.mask == mask) {
-      *out = e.schedule;
-      return DASH_OK;
-    }
-  const int grid = dev->cus * blocks_per_cu(*dev, D, L.T, mask);
-  if (grid <= 0) return DASH_ERR_HIP;
-  // every deterministic schedule that applies, each with its own split of
-  // the query heads (a split group simulates as `parts` groups of G/parts
-  // heads, in the same dispatch order); the shortest critical path wins,
-  // ties to the earlier of SYMMETRIC_SHIFT, SHIFT, DESCENDING_Q, NAIVE
+  if (grid <= 0) return DASH_ERR_SHAPE;
+  const int G = Hq / Hkv;
   int sched = -1;
+  double best = 0.0;
   {
     static const int order[4] = {DASH_SCHED_SYMMETRIC_SHIFT, DASH_SCHED_SHIFT, DASH_SCHED_DESCENDING_Q,
                                  DASH_SCHED_NAIVE};
-    const int G = Hq / Hkv;
-    double best = 0.0;
     st = DASH_OK;
     for (int s : order) {
       if (s == DASH_SCHED_SYMMETRIC_SHIFT && (mask != DASH_MASK_CAUSAL || L.N % 2 != 0)) continue;
@@ -249,14 +259,95 @@ int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
     const bool sym_ok = mask == DASH_MASK_CAUSAL && L.N % 2 == 0 &&
                         dash::items_per_group(mask, DASH_SCHED_SYMMETRIC_SHIFT, L.N) <= grid;
     const bool shift_ok = dash::items_per_group(mask, DASH_SCHED_SHIFT, L.N) <= grid;
-    sched = sym_ok ? DASH_SCHED_SYMMETRIC_SHIFT
-                   : shift_ok ? DASH_SCHED_SHIFT
-                              : mask == DASH_MASK_CAUSAL ? DASH_SCHED_DESCENDING_Q : DASH_SCHED_NAIVE;
-  } else if (st != DASH_OK) {
-    return st;
+    *out = sym_ok ? DASH_SCHED_SYMMETRIC_SHIFT
+                  : shift_ok ? DASH_SCHED_SHIFT
+                             : mask == DASH_MASK_CAUSAL ? DASH_SCHED_DESCENDING_Q : DASH_SCHED_NAIVE;
+    return DASH_OK;
   }
-  g_auto.push_back({dev_id, B, Hq, Hkv, S, D, mask, sched});
+  if (st != DASH_OK) return st;
   *out = sched;
+  const long long per_group = dash_schedule_table_tasks(mask, L.N, G);
+  const bool same_workspace =
+      L.T != 256 || G == 1 || head_parts(B, Hkv, G, L.N, L.T, mask, DASH_SCHED_AUTO) == G;
+  if (!allow_table || !same_workspace || per_group <= 0 || per_group * B * Hkv > kAutoTableSimTasks)
+    return DASH_OK;
+  std::vector<int> offs((size_t)G * L.N + 1), tasks((size_t)per_group * 4);
+  int n_items = 0;
+  dash_sim_result res;
+  st = dash_schedule_search(S, D, mask, G, B * Hkv, grid, kAutoC, kAutoCDiag, kAutoR, &n_items, offs.data(),
+                            tasks.data(), nullptr, &res);
+  // no candidate runs on this grid, or none beats the closed forms
+  if (st != DASH_OK || res.deadlock || !(res.makespan < best)) return DASH_OK;
+  int pst = DASH_OK;
+  const size_t bytes =
+      dash_schedule_table_pack(S, D, mask, G, n_items, offs.data(), tasks.data(), nullptr, 0, &pst);
+  // the AUTO layout's table region holds the largest table of the shape
+  Layout LA;
+  if (pst != DASH_OK || make_layout(B, Hq, Hkv, S, D, mask, DASH_SCHED_AUTO, &LA) != DASH_OK ||
+      bytes > LA.table_bytes)
+    return DASH_OK;
+  packed->resize(bytes);
+  dash_schedule_table_pack(S, D, mask, G, n_items, offs.data(), tasks.data(), packed->data(), bytes, &pst);
+  if (pst != DASH_OK) return DASH_OK;
+  *items = n_items;
+  *out = DASH_SCHED_TABLE;
+  return DASH_OK;
+}
+
+// AUTO's resolution for a shape on a device: the schedule, and for the
+// searched table its device form in pinned host memory (held until the
+// process ends), copied into the workspace by every prepare phase.
+struct AutoChoice {
+  int schedule = DASH_SCHED_NAIVE;
+  const void* table = nullptr;
+  size_t table_bytes = 0;
+  int items = 0;
+};
+
+struct AutoEntry {
+  int dev, B, Hq, Hkv, S, D, mask;
+  bool allow_table;
+  AutoChoice choice;
+};
+std::vector<AutoEntry> g_auto;
+std::mutex g_auto_mu;
+
+// Resolves DASH_SCHED_AUTO for a shape on the current device (cached).
+int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, bool allow_table, AutoChoice* out) {
+  int st = check_shape(B, Hq, Hkv, S, D, mask, DASH_SCHED_NAIVE);
+  if (st != DASH_OK) return st;
+  if (B == 0 || S == 0) {
+    *out = AutoChoice();
+    return DASH_OK;
+  }
+  DeviceInfo* dev = nullptr;
+  st = device_info(&dev);
+  if (st != DASH_OK) return st;
+  int dev_id = 0;
+  if (hipGetDevice(&dev_id) != hipSuccess) return DASH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_auto_mu);
+  for (const AutoEntry& e : g_auto)
+    if (e.dev == dev_id && e.B == B && e.Hq == Hq && e.Hkv == Hkv && e.S == S && e.D == D &&
+        e.mask == mask && e.allow_table == allow_table) {
+      *out = e.choice;
+      return DASH_OK;
+    }
+  const int T = dash_attn_tile_size(S, D);
+  const int grid = dev->cus * blocks_per_cu(*dev, D, T, mask);
+  if (grid <= 0) return DASH_ERR_HIP;
+  AutoChoice c;
+  std::vector<unsigned char> packed;
+  st = auto_decide(B, Hq, Hkv, S, D, mask, grid, allow_table, &c.schedule, &packed, &c.items);
+  if (st != DASH_OK) return st;
+  if (c.schedule == DASH_SCHED_TABLE) {
+    void* host = nullptr;
+    if (hipHostMalloc(&host, packed.size(), hipHostMallocDefault) != hipSuccess) return DASH_ERR_HIP;
+    std::memcpy(host, packed.data(), packed.size());
+    c.table = host;
+    c.table_bytes = packed.size();
+  }
+  g_auto.push_back({dev_id, B, Hq, Hkv, S, D, mask, allow_table, c});
+  *out = c;
   return DASH_OK;
 }
 
@@ -265,8 +356,15 @@ int auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask, int* out) {
 extern "C" {
 
 int dash_attn_bwd_auto_schedule(int B, int Hq, int Hkv, int S, int D, int mask) {
-  int sched = 0;
-  const int st = auto_schedule(B, Hq, Hkv, S, D, mask, &sched);
+  AutoChoice c;
+  const int st = auto_schedule(B, Hq, Hkv, S, D, mask, true, &c);
+  return st == DASH_OK ? c.schedule : -st;
+}
+
+int dash_attn_bwd_auto_schedule_on(int B, int Hq, int Hkv, int S, int D, int mask, int grid) {
+  int sched = 0, items = 0;
+  std::vector<unsigned char> packed;
+  const int st = auto_decide(B, Hq, Hkv, S, D, mask, grid, true, &sched, &packed, &items);
   return st == DASH_OK ? sched : -st;
 }
 
@@ -358,6 +456,11 @@ struct TableArgs {
 struct BwdPlan {
   Layout L;
   int grid = 0;
+  // AUTO resolved to the searched table: its pinned host copy, copied into
+  // the workspace's table region by the prepare phase
+  const void* upload_src = nullptr;
+  void* upload_dst = nullptr;
+  size_t upload_bytes = 0;
   dash::PreParams pp;
   dash::BwdParams bp;
   dash::FinParams fp;
@@ -371,7 +474,7 @@ struct BwdPlan {
 int plan_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
              int D, int mask, int schedule, void* workspace, size_t workspace_bytes, int need,
-             BwdPlan* P, bool* empty, const TableArgs* tab = nullptr) {
+             BwdPlan* P, bool* empty, const TableArgs* tab = nullptr, bool allow_table = true) {
   *empty = false;
   int st = check_shape(B, Hq, Hkv, S, D, mask, schedule);
   if (st != DASH_OK) return st;
@@ -395,12 +498,24 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
     return DASH_ERR_WORKSPACE;
 
+  TableArgs auto_tab;
   if (schedule == DASH_SCHED_AUTO) {
-    st = auto_schedule(B, Hq, Hkv, S, D, mask, &schedule);
+    AutoChoice c;
+    st = auto_schedule(B, Hq, Hkv, S, D, mask, allow_table, &c);
     if (st != DASH_OK) return st;
+    schedule = c.schedule;
+    const size_t table_off = L.table;
     // the resolved schedule's layout: the same offsets, at most as many parts
+    // (a searched table is chosen only where it has as many as AUTO)
     st = make_layout(B, Hq, Hkv, S, D, mask, schedule, &L);
     if (st != DASH_OK) return st;
+    if (schedule == DASH_SCHED_TABLE) {
+      auto_tab = {(char*)workspace + table_off, c.items, 0};
+      tab = &auto_tab;
+      P->upload_src = c.table;
+      P->upload_dst = (char*)workspace + table_off;
+      P->upload_bytes = c.table_bytes;
+    }
   }
   DeviceInfo* dev = nullptr;
   st = device_info(&dev);
@@ -507,6 +622,17 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return DASH_OK;
 }
 
+// The prepare phase: the preprocess, and the searched table's copy into the
+// workspace when AUTO resolved to it (from pinned host memory, so the copy is
+// asynchronous and may be captured).
+int launch_prepare(const BwdPlan& P, hipStream_t s) {
+  if (dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
+  if (P.upload_bytes &&
+      hipMemcpyAsync(P.upload_dst, P.upload_src, P.upload_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+    return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
 int launch_main_phase(const BwdPlan& P, int D, int mask, hipStream_t s) {
   const bool causal = mask == DASH_MASK_CAUSAL;
   if (P.L.T == 256) {
@@ -557,7 +683,26 @@ int table_phases(const void* q, const void* k, const void* v, const void* o, con
                 workspace_bytes, phases, &P, &empty, &tab);
   if (st != DASH_OK || empty) return st;
   hipStream_t s = (hipStream_t)stream;
-  if ((phases & 1) && dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
+  if (phases & 1) {
+    st = launch_prepare(P, s);
+    if (st != DASH_OK) return st;
+  }
+  return launch_main_phase(P, D, mask, s);
+}
+
+// dash_attn_bwd; `allow_table` = false keeps AUTO among the closed forms
+// (no pinned host memory is allocated), for dash_attn_bwd_noalloc.
+int bwd_all(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, int mask, int schedule,
+            void* workspace, size_t workspace_bytes, void* stream, bool allow_table) {
+  BwdPlan P;
+  bool empty = false;
+  int st = plan_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule, workspace,
+                    workspace_bytes, 3, &P, &empty, nullptr, allow_table);
+  if (st != DASH_OK || empty) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_prepare(P, s);
+  if (st != DASH_OK) return st;
   return launch_main_phase(P, D, mask, s);
 }
 
@@ -569,14 +714,8 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
                   int D, int mask, int schedule, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  BwdPlan P;
-  bool empty = false;
-  int st = plan_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule,
-                    workspace, workspace_bytes, 3, &P, &empty);
-  if (st != DASH_OK || empty) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (dash::launch_preprocess(P.pp, s) != hipSuccess) return DASH_ERR_HIP;
-  return launch_main_phase(P, D, mask, s);
+  return bwd_all(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule, workspace,
+                 workspace_bytes, stream, true);
 }
 
 int dash_attn_bwd_prepare(const void* o, const void* dout, const float* lse, int B, int Hq,
@@ -587,8 +726,7 @@ int dash_attn_bwd_prepare(const void* o, const void* dout, const float* lse, int
   int st = plan_bwd(nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr, B, Hq,
                     Hkv, S, D, mask, schedule, workspace, workspace_bytes, 1, &P, &empty);
   if (st != DASH_OK || empty) return st;
-  if (dash::launch_preprocess(P.pp, (hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
-  return DASH_OK;
+  return launch_prepare(P, (hipStream_t)stream);
 }
 
 int dash_attn_bwd_run(const void* q, const void* k, const void* v, const void* dout, void* dq,
@@ -633,12 +771,12 @@ int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const voi
   if (L.total > dash::kScratchBytes) return DASH_ERR_WORKSPACE;
   // an empty problem launches nothing and never looks at the workspace
   if (B == 0 || S == 0)
-    return dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule,
-                         nullptr, 0, stream);
+    return bwd_all(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule, nullptr, 0, stream,
+                   false);
   void* ws = nullptr;
   if (dash::scratch_workspace(&ws) != hipSuccess) return DASH_ERR_HIP;
-  return dash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule, ws,
-                       dash::kScratchBytes, stream);
+  return bwd_all(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, S, D, mask, schedule, ws, dash::kScratchBytes,
+                 stream, false);
 }
 
 int dash_attn_bwd_check(const void* workspace, void* stream) {

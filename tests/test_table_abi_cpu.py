@@ -241,8 +241,12 @@ def test_table_workspace_holds_per_head_partials():
     # one head per group, or small tiles: no partials
     assert dash.dash_attn_bwd_head_parts(1, 4, 4, 4096, 128, 0, dash.TABLE) == 1
     assert dash.dash_attn_bwd_head_parts(1, 4, 2, 512, 128, 0, dash.TABLE) == 1
+    # beyond the closed forms' workspace: room for the largest table (the one
+    # AUTO may resolve to), 8 header words, 6 offset words and 2 words per
+    # task of the 16 full-mask tasks, rounded to 256 bytes
+    words = 8 + ((4 + 2) & ~1) + 2 * 16
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 0, dash.TABLE) == \
-        dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 0, dash.NAIVE)
+        dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64, 0, dash.NAIVE) + ((4 * words + 255) & ~255)
 
 
 FAMILY_CASES = [(m, N, G, kind, order, block)
@@ -333,3 +337,64 @@ def test_search_packs_grouped_heads():
     assert dash.dash_attn_tile_size(512, 128) == 128
     got2 = dash.dash_schedule_search(512, 128, m, G, groups, P, c, cd, r)
     assert got2["family"][0] != dash.FAMILY_PACKED
+
+
+AUTO_CASES = [
+    # B, Hq, Hkv, S, D, mask, grid
+    (1, 28, 4, 4096, 128, sch.CAUSAL, 256),   # closed forms split 7 heads into 7 parts
+    (2, 14, 2, 4096, 128, sch.CAUSAL, 256),
+    (1, 28, 4, 2048, 128, sch.CAUSAL, 256),
+    (2, 6, 2, 4096, 128, sch.CAUSAL, 256),
+    (4, 32, 8, 4096, 128, sch.CAUSAL, 256),   # whole-tile items only
+    (1, 8, 4, 8192, 128, sch.CAUSAL, 256),
+    (1, 4, 4, 2048, 128, sch.FULL, 64),
+    (1, 28, 4, 512, 128, sch.CAUSAL, 256),    # 128-key tiles
+    (1, 14, 2, 4096, 64, sch.CAUSAL, 128),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,m,grid", AUTO_CASES)
+def test_auto_choice_equals_oracle(B, Hq, Hkv, S, D, m, grid):
+    # the closed forms simulated by the oracle with the library's head parts,
+    # then the oracle's search where the table needs no more workspace; the
+    # table wins only with a strictly shorter critical path
+    from oracle import dag
+    T = dash.dash_attn_tile_size(S, D)
+    N = (S + T - 1) // T
+    G = Hq // Hkv
+    groups = B * Hkv
+    passes = 8 if (T, D) == (256, 128) else 4 if T == 256 or (T, D) == (128, 128) else 2
+    best = None
+    for s in (sch.SYMMETRIC_SHIFT, sch.SHIFT, sch.DESCENDING_Q, sch.NAIVE):
+        if s == sch.SYMMETRIC_SHIFT and (m != sch.CAUSAL or N % 2):
+            continue
+        parts = dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, m, s)
+        rep = dag.simulate(s, m, N, G=G // parts, groups=groups * parts, P=grid, dispatch="dynamic",
+                           c=1.0, c_diag=1.0, r=0.1)
+        if rep["deadlock"]:
+            continue
+        if best is None or rep["makespan"] < best[1]:
+            best = (s, rep["makespan"])
+    want = best[0]
+    same_ws = T != 256 or G == 1 or dash.dash_attn_bwd_head_parts(B, Hq, Hkv, S, D, m, dash.AUTO) == G
+    if same_ws and groups * G * se.tiles(m, N) <= 1 << 18:
+        found = se.search(m, N, G, groups, grid, passes, 1.0, 1.0, 0.1, T == 256)
+        if found is not None:
+            # a tie (the search returning a closed form) keeps the closed form
+            if found[3]["makespan"] < best[1] - 1e-9:
+                want = dash.TABLE
+    assert dash.dash_attn_bwd_auto_schedule_on(B, Hq, Hkv, S, D, m, grid) == want
+
+
+def test_auto_choice_picks_the_table_where_the_closed_forms_leave_units_idle():
+    # on 256 workgroups: the 16k causal layer with 7 heads per KV head runs the
+    # packed per-head table, the 8B layer the symmetric shift, the full-mask
+    # 16k layer the shift; no table where it would need more workspace
+    assert dash.dash_attn_bwd_auto_schedule_on(1, 28, 4, 16384, 128, 1, 256) == dash.TABLE
+    assert dash.dash_attn_bwd_auto_schedule_on(4, 32, 8, 4096, 128, 1, 256) == dash.SYMMETRIC_SHIFT
+    assert dash.dash_attn_bwd_auto_schedule_on(1, 32, 32, 16384, 128, 0, 256) == dash.SHIFT
+    assert dash.dash_attn_bwd_auto_schedule_on(2, 24, 24, 4096, 64, 0, 256) == dash.SHIFT
+    assert dash.dash_attn_bwd_auto_schedule_on(0, 28, 4, 4096, 128, 1, 256) == dash.NAIVE  # empty
+    with pytest.raises(dash.DashError) as e:
+        dash.dash_attn_bwd_auto_schedule_on(1, 28, 4, 4096, 128, 1, 0)
+    assert e.value.status == dash.DASH_ERR_SHAPE
