@@ -318,6 +318,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_main_wide(BwdParams p) {
   if (split && blockIdx.x == 0 && tid == 0)
     __hip_atomic_store(p.ctrl + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (blockIdx.x == 0 && tid == 0) clock_stamp(p.ctrl + 8);
+  // the older wave of each SIMD's pair (waves 0-3) issues first: the
+  // hardware already favours it, and letting it run further ahead gets its
+  // memory requests out earlier (measured 0.5-3 % faster on the best
+  // schedules; raising waves 4-7 instead was slower)
+  if (w < C::NW / 2) __builtin_amdgcn_s_setprio(3);
   for (;;) {
     __syncthreads();
     int* const misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
