@@ -1,6 +1,7 @@
 """Run-to-run bit identity at the full workload sizes, 20 runs per schedule.
 
-Every deterministic schedule of the four large workloads (an 8B-Llama-shaped
+Every deterministic schedule (and AUTO where it resolves to the searched
+task table) of the four large workloads (an 8B-Llama-shaped
 causal layer, a diffusion/vision full-mask block, a 16k full-mask layer and a
 7B-Qwen-shaped 16k causal layer) runs 20 times on the whole problem in the
 launch configuration the benchmark times.  The runs rotate over three streams
@@ -37,10 +38,14 @@ WORKLOADS = {
 }
 
 
-def _schedules(causal, N):
+def _schedules(causal, N, shape):
     out = [dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT]
     if causal and N % 2 == 0:
         out.append(dash.SYMMETRIC_SHIFT)
+    # AUTO where it runs the searched task table
+    B, Hq, Hkv, S, D = shape
+    if dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, int(causal)) == dash.TABLE:
+        out.append(dash.AUTO)
     return out
 
 
@@ -60,7 +65,7 @@ def test_fullsize_bit_identical_over_20_runs(name):
     dq = torch.empty_like(x["q"])
     dk = torch.empty_like(x["k"])
     dv = torch.empty_like(x["v"])
-    for sched in _schedules(causal, N):
+    for sched in _schedules(causal, N, (B, Hq, Hkv, S, D)):
         print("  schedule", sched, flush=True)
         rng = random.Random(4321 + sched)
         ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)

@@ -1,7 +1,7 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
-For each large configuration every applicable schedule runs on the whole
-problem; the float64 oracle is evaluated for one sampled (batch, kv head)
+For each large configuration every applicable schedule (and AUTO where it
+resolves to the searched task table) runs on the whole problem; the float64 oracle is evaluated for one sampled (batch, kv head)
 group -- all of its query heads, so dK/dV of that kv head are complete -- and
 compared element by element.  The rest of the output is checked through
 properties that hold at any size: finite values and, for the deterministic
@@ -31,10 +31,15 @@ CONFIGS = {
 }
 
 
-def _schedules(causal, N):
+def _schedules(causal, N, shape):
     out = [dash.NAIVE, dash.DESCENDING_Q, dash.SHIFT, dash.ATOMIC]
     if causal and N % 2 == 0:
         out.append(dash.SYMMETRIC_SHIFT)
+    # AUTO where it runs the searched table (the schedule bench.py reports
+    # for the 16k causal layer with 7 heads per KV head on 256 compute units)
+    B, Hq, Hkv, S, D = shape
+    if dash.dash_attn_bwd_auto_schedule(B, Hq, Hkv, S, D, int(causal)) == dash.TABLE:
+        out.append(dash.AUTO)
     return out
 
 
@@ -52,7 +57,7 @@ def test_fullsize_sampled_parity(name):
     h = {k: gu.host64(v[sb:sb + 1]) for k, v in x.items()}
     ref = oa.attention_backward_sampled(h["q"], h["k"], h["v"], h["do"], causal, [skv])[skv]
     rdq, rdk, rdv = ref
-    for sched in _schedules(causal, N):
+    for sched in _schedules(causal, N, (B, Hq, Hkv, S, D)):
         print("  schedule", sched, flush=True)
         ws = dash.new_workspace(x["q"], x["k"], int(causal), sched)
         dq, dk, dv = gu.run_backward(x, o, lse, causal, sched, workspace=ws)
