@@ -403,3 +403,23 @@ def test_search_packs_grouped_heads():
     offs2, tasks2, fam2, rep2 = se.search(m, N, G, groups, P, 8, 1.0, 0.5, 0.125, head_form_ok=False)
     assert fam2[0] != se.PACKED
     assert rep["makespan"] < rep2["makespan"]
+
+
+GOLDEN_PACKED = os.path.join(os.path.dirname(__file__), "golden", "packed_tables.json")
+
+
+def _golden_items(items):
+    offs, tasks = [0], []
+    for text in items:
+        tasks.extend(tuple(int(x) for x in tok.split(",")) for tok in text.split())
+        offs.append(len(tasks))
+    return offs, tasks
+
+
+@pytest.mark.parametrize("k", range(2))
+def test_packed_kind_equals_the_hand_written_tables(k):
+    case = json.load(open(GOLDEN_PACKED))["cases"][k]
+    mask = sch.CAUSAL if case["mask"] == "causal" else sch.FULL
+    offs, tasks = se.packed_table(mask, case["N"], case["G"], case["bins"])
+    assert (offs, tasks) == _golden_items(case["items"])
+    assert se.structure_ok(mask, case["N"], case["G"], offs, tasks)
