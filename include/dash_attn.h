@@ -25,8 +25,13 @@
  *
  * Ownership: the caller owns every buffer, including the workspace (size from
  * dash_attn_bwd_workspace_size).  The library allocates no device memory; it
- * caches the device's compute-unit count and the kernels' occupancy.  Calls
- * are asynchronous on the given HIP stream (NULL = default stream).
+ * caches the device's compute-unit count and the kernels' occupancy, and
+ * DASH_SCHED_AUTO's choice per device and shape (with, where that choice is
+ * the searched task table, the table's device form in pinned host memory,
+ * allocated on the shape's first AUTO call and held until the process ends;
+ * dash_attn_bwd_noalloc never makes that choice).  The caches are guarded by
+ * locks.  Calls are asynchronous on the given HIP stream (NULL = default
+ * stream).
  *
  * Errors: every argument is checked on the host before anything is enqueued;
  * a non-zero status means nothing was launched.  A failed kernel launch
