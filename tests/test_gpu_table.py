@@ -11,6 +11,9 @@
   tile, dK/dV summed over fp32 per-head partials) against the float64
   oracle, with counters, a bitwise rerun, and a whole-tile table run next on
   the same workspace (the per-head mark does not outlive its run).
+* 12 seeded random tables (shuffled walks, run order and item cuts, whole-tile
+  and per-head runs, full and capped grids) that pass the host check match
+  the oracle, end their counters right and rerun bit for bit.
 * The kernel refuses a table made for another kernel, and a launch narrower
   than the table's widest dispatch block: nothing is written and
   dash_attn_bwd_check reports DASH_ERR_TABLE (the kernels return before any
@@ -304,3 +307,98 @@ def test_kernel_refuses_a_grid_narrower_than_a_block():
         dash.dash_attn_bwd_table(x["q"], x["k"], x["v"], o, x["do"], lse, dq, dk, dv, 0, table,
                                  items, 1 << 20, ws)
     assert e.value.status == dash.DASH_ERR_SHAPE
+
+
+def _random_table(mask, N, G, rng, per_head):
+    """Seeded random table: shuffled walks, whole-tile or per-head runs in a
+    shuffled order, random item cuts, ranks in the order the walks reach each
+    dQ tile (position, then item)."""
+    from oracle import schedule as sch
+    chains = []
+    for i in range(N):
+        js = [j for j in range(N) if sch.valid(mask, i, j)]
+        if per_head:
+            for g in range(G):
+                w = list(js)
+                rng.shuffle(w)
+                chains.append([(g, i, j) for j in w])
+        else:
+            rng.shuffle(js)
+            chains.append([(g, i, j) for j in js for g in range(G)])
+    rng.shuffle(chains)
+    items, cur = [], []
+    for x, ch in enumerate(chains):
+        cur.extend(ch)
+        if x == len(chains) - 1 or rng.random() < 0.5:
+            items.append(cur)
+            cur = []
+    order = {}
+    for k, lst in enumerate(items):
+        for pos, (g, i, j) in enumerate(lst):
+            order.setdefault((g, j), []).append((pos, k, i))
+    rank = {}
+    for (g, j), lst in order.items():
+        for r, (_, _, i) in enumerate(sorted(lst)):
+            rank[(g, i, j)] = r
+    offs, tasks = [0], []
+    for lst in items:
+        tasks.extend((g, i, j, rank[(g, i, j)]) for (g, i, j) in lst)
+        offs.append(len(tasks))
+    return offs, tasks
+
+
+RANDOM_CASES = [
+    # B, S, Hq, Hkv, D, causal, grid (0 = the device's)
+    (1, 256, 2, 1, 64, True, 0),       # 64-key tiles
+    (1, 300, 3, 1, 64, False, 4),      # ragged, capped grid
+    (2, 512, 4, 2, 128, True, 0),      # 128-key tiles
+    (1, 1024, 4, 2, 128, False, 0),    # 256-key tiles
+    (1, 1300, 6, 2, 128, True, 0),     # ragged
+    (1, 2048, 6, 2, 64, True, 0),
+    (2, 1024, 3, 1, 64, False, 6),
+    (1, 2048, 4, 2, 128, False, 8),
+    (1, 1800, 3, 3, 128, True, 0),     # one head per group
+    (1, 2048, 6, 2, 128, True, 5),
+    (2, 1500, 4, 1, 64, True, 0),
+    (1, 1024, 8, 2, 128, True, 3),
+]
+
+
+@pytest.mark.parametrize("k", range(len(RANDOM_CASES)))
+def test_random_valid_tables_parity(k):
+    # random tables that pass the host check run to the oracle's result, end
+    # every turn counter at its contributor count and rerun bit for bit;
+    # per-head runs wherever the 256-key kernels and G > 1 allow them
+    import random
+    B, S, Hq, Hkv, D, causal, grid = RANDOM_CASES[k]
+    T, N = _tiles(S, D)
+    G = Hq // Hkv
+    mask = int(causal)
+    rng = random.Random(7000 + k)
+    P = grid or dash.dash_attn_bwd_grid_size(S, D, mask)
+    for _ in range(50):
+        per_head = T == 256 and G > 1 and rng.random() < 0.6
+        offs, tasks = _random_table(mask, N, G, rng, per_head)
+        if dash.dash_schedule_table_check(S, D, mask, G, P, offs, tasks) == dash.DASH_OK:
+            break
+    else:
+        pytest.fail("no valid random table in 50 draws")
+    print("random table", RANDOM_CASES[k], "per-head", per_head, "items", len(offs) - 1, flush=True)
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=5700 + k)
+    h = {kk: gu.host64(v) for kk, v in x.items()}
+    refs = oa.attention_backward(h["q"], h["k"], h["v"], h["do"], causal)
+    o, lse = gu.run_forward(x, causal)
+    table, items = dash.upload_table(x["q"], x["k"], causal, offs, tasks)
+    ws = dash.new_workspace(x["q"], x["k"], mask, dash.TABLE)
+    out = [t.clone() for t in dash.backward_table(x["q"], x["k"], x["v"], o, x["do"], lse, causal, table,
+                                                  items, grid=grid, workspace=ws)]
+    for name, got, ref in zip(("dq", "dk", "dv"), out, refs):
+        e = gu.errors(gu.host64(got), ref)
+        print("  %s rel-l2 %.3e max-abs(excess) %.3e max-abs %.3e" % ((name,) + e))
+        assert gu.within(e), (name, e)
+    cnt = gu.read_counters(ws, B, Hq, S, D)
+    assert np.array_equal(cnt, gu.expected_counters(B, Hq, S, D, causal))
+    again = dash.backward_table(x["q"], x["k"], x["v"], o, x["do"], lse, causal, table, items, grid=grid,
+                                workspace=ws)
+    for a, b in zip(out, again):
+        assert _same(a, b)
