@@ -166,6 +166,8 @@ PACKED = [
     (2, 1900, 6, 2, 64, True, 12),    # D = 64, ragged last tile, G = 3
     (1, 2048, 4, 1, 128, False, 6),   # full mask, G = 4 on 6 workgroups
     (1, 3000, 7, 1, 128, True, 20),   # seven heads per group, ragged, N = 12
+    (1, 2048, 16, 2, 128, True, 32),  # eight heads per group: eight partial slots
+    (3, 1536, 6, 2, 64, False, 24),   # three batches, D = 64, full mask
 ]
 
 
