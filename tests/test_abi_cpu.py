@@ -439,3 +439,24 @@ def test_library_split_items_equal_oracle(s, m, N, G, parts):
         for step, (g, i, j) in enumerate(it):
             gl, il, jl, rl = dash.dash_schedule_task(m, s, N, Gp, b, step)
             assert (k * Gp + gl, il, jl, rl) == (g, i, j, rk[(g, i, j)]), (n, step)
+
+
+def test_bench_searched_table_row(monkeypatch):
+    """bench.py's table row on a 256-workgroup grid (the MI355X's, set here
+    since no device is present): the search returns exactly a closed form
+    that splits no heads for four workloads, which the line names instead of
+    timing it twice, and the packed per-head table for the 16k causal layer
+    with seven heads per KV head."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    monkeypatch.setattr(dash, "dash_attn_bwd_grid_size", lambda S, D, mask: 256)
+    want = {"long_full": "shift", "llama8b_causal": "symmetric_shift", "dit_full": "shift",
+            "qwen7b_causal": None}
+    for name, same in want.items():
+        t = bench.searched_table(dash, bench.CONFIGS[name])
+        assert t["same_as"] == same, (name, t["family"])
+        if name == "qwen7b_causal":
+            assert t["per_head"] and t["family"][0] == dash.FAMILY_PACKED
+            assert t["items"] == 64
+        else:
+            assert not t["per_head"]
