@@ -14,6 +14,7 @@
 * 12 seeded random tables (shuffled walks, run order and item cuts, whole-tile
   and per-head runs, full and capped grids) that pass the host check match
   the oracle, end their counters right and rerun bit for bit.
+* The 128-key kernel refuses a header forged to claim the per-head form.
 * The kernel refuses a table made for another kernel, and a launch narrower
   than the table's widest dispatch block: nothing is written and
   dash_attn_bwd_check reports DASH_ERR_TABLE (the kernels return before any
@@ -285,6 +286,31 @@ def test_kernel_refuses_a_table_for_another_kernel():
                               workspace=ws)
     ref = gu.run_backward(x, o, lse, causal, dash.NAIVE)
     assert _same(got[0], ref[0])
+
+
+def test_kernel_refuses_a_per_head_flag_on_small_tiles():
+    # a valid whole-tile table for 128-key tiles whose header is altered to
+    # claim the per-head form: that kernel has no per-head partials, so it
+    # refuses the table before any work and writes nothing
+    B, S, Hq, Hkv, D, causal = 1, 512, 4, 2, 128, True
+    T, N = _tiles(S, D)
+    assert T == 128
+    offs, tasks = dash.dash_schedule_table_closed_form(1, dash.NAIVE, N, 2)
+    raw = bytearray(dash.dash_schedule_table_pack(S, D, 1, 2, offs, tasks))
+    raw[12:16] = (int.from_bytes(raw[12:16], "little") | 0x100).to_bytes(4, "little")
+    table = torch.frombuffer(raw, dtype=torch.uint8).cuda()
+    x = gu.gpu_inputs(B, S, Hq, Hkv, D, seed=5800)
+    o, lse = gu.run_forward(x, causal)
+    dq, dk, dv = _sentinel_outputs(x)
+    ws = dash.new_workspace(x["q"], x["k"], 1, dash.TABLE)
+    print("refused table: per-head flag on 128-key tiles", flush=True)
+    dash.dash_attn_bwd_table(x["q"], x["k"], x["v"], o, x["do"], lse, dq, dk, dv, 1, table,
+                             len(offs) - 1, 0, ws)
+    with pytest.raises(dash.DashError) as e:
+        dash.dash_attn_bwd_check(ws)
+    assert e.value.status == dash.DASH_ERR_TABLE
+    for t in (dq, dk, dv):
+        assert torch.all(t == 7.0)
 
 
 def test_kernel_refuses_a_grid_narrower_than_a_block():
