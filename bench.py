@@ -406,7 +406,10 @@ def sim_report():
     measure on), dynamic dispatch, c = c_diag = 1, r/c in {0, 0.1, 0.25}.
     Each schedule runs with the query-head split the library gives it (a
     split group simulates as `parts` groups of G / parts heads, in the same
-    dispatch order).  One line of JSON per case."""
+    dispatch order).  A last row per case is the searched table
+    (dash_schedule_search with the same weights; schedule "table", with its
+    family and whether it is in the per-head form).  One line of JSON per
+    case."""
     import scheduling_persistent_attn_amd as dash
     names = {v: k for k, v in dash.SCHEDULES.items()}
     for name in ("llama8b_causal", "dit_full", "long_full", "qwen7b_causal"):
@@ -432,6 +435,19 @@ def sim_report():
                                       "lemma1_violations": res["violations"],
                                       "order_edges": res["order_edges"],
                                       "deadlock": bool(res["deadlock"])}), flush=True)
+                tab = dash.dash_schedule_search(cfg["S"], cfg["D"], mask, G, groups, P, 1.0, 1.0, r)
+                raw = dash.dash_schedule_table_pack(cfg["S"], cfg["D"], mask, G, tab["item_offsets"],
+                                                    tab["tasks"])
+                rep = tab["report"]
+                print(json.dumps({"workload": name, "N": N, "G": G, "groups": groups,
+                                  "P": P, "r_over_c": r, "schedule": "table",
+                                  "family": list(tab["family"]),
+                                  "per_head": bool(struct.unpack_from("<I", raw, 12)[0] & 0x100),
+                                  "critical_path": rep["makespan"],
+                                  "efficiency": rep["efficiency"],
+                                  "lemma1_violations": rep["violations"],
+                                  "order_edges": rep["order_edges"],
+                                  "deadlock": bool(rep["deadlock"])}), flush=True)
 
 
 def trace_report(dash, name):

@@ -325,8 +325,20 @@ def test_sim_report_closed_forms(capsys):
     import bench
     bench.sim_report()
     rows = [json.loads(l) for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
-    assert len(rows) == 84
+    assert len(rows) == 84 + 24  # closed forms, then one searched table per case
     pick = {(r["workload"], r["P"], r["r_over_c"], r["schedule"]): r for r in rows}
+    # the searched table is never longer than the best closed form of its case
+    for (w, P, r, sname), row in pick.items():
+        if sname != "table":
+            continue
+        assert not row["deadlock"]
+        best = min(v["critical_path"] for (w2, P2, r2, s2), v in pick.items()
+                   if (w2, P2, r2) == (w, P, r) and s2 != "table" and not v["deadlock"]
+                   and v["head_parts"] == 1)
+        assert row["critical_path"] <= best + 1e-9
+    q = pick[("qwen7b_causal", 256, 0.1, "table")]
+    assert q["family"][0] == dash.FAMILY_PACKED and q["per_head"]
+    assert q["critical_path"] < pick[("qwen7b_causal", 256, 0.1, "symmetric_shift")]["critical_path"]
     for s in ("naive", "descending_q", "shift"):
         assert pick[("dit_full", 256, 0.0, s)]["critical_path"] == 48.0
     assert dash.dash_attn_tile_size(4096, 64) == 256
