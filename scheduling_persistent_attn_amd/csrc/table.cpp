@@ -412,7 +412,8 @@ int packed_bins(int N, int G, int groups, int P) {
 // at which the unit reaches j, unit position) -- lockstep arrival inside a
 // block, blocks one after another.
 GroupTable family_table(int mask, int N, int G, int kind, int order, int block) {
-  if (kind == DASH_FAMILY_PACKED) return packed_table(mask, N, G, std::max(1, block));
+  // more bins than chains leave the extra ones empty: the same table
+  if (kind == DASH_FAMILY_PACKED) return packed_table(mask, N, G, std::max(1, std::min(block, G * N)));
   const int units = kind == DASH_FAMILY_SYMMETRIC ? N / 2 : N;
   std::vector<std::vector<std::pair<int, int>>> walks(units);
   std::vector<int> unit_of(units);
@@ -490,6 +491,7 @@ int dash_schedule_table_family(int mask, int N, int G, int kind, int order, int 
   if (!items || !item_offsets || !tasks) return DASH_ERR_NULL;
   if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return DASH_ERR_SCHEDULE_MASK;
   if (N < 1 || G < 1 || block < 1 || (order != 0 && order != 1)) return DASH_ERR_SHAPE;
+  if (kind == DASH_FAMILY_PACKED && order != 0) return DASH_ERR_SHAPE;  // one order only
   if (!dash::family_applies(mask, N, kind)) return DASH_ERR_SCHEDULE_MASK;
   if ((long long)G * dash::table_tiles(mask, N) > dash::kMaxTableTasks) return DASH_ERR_UNSUPPORTED;
   write_table(dash::family_table(mask, N, G, kind, order, block), items, item_offsets, tasks);

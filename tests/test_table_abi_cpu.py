@@ -277,6 +277,14 @@ def test_family_arguments():
              dash._iptr(t)) != dash.DASH_OK
     assert f(sch.CAUSAL, 4, 1, 9, 0, 1, ctypes.byref(items), dash._iptr(o),
              dash._iptr(t)) != dash.DASH_OK
+    # the packed kind has one order; a bin count beyond the walks gives the
+    # table of one walk per item (and allocates nothing for the rest)
+    assert f(sch.CAUSAL, 4, 2, dash.FAMILY_PACKED, 1, 2, ctypes.byref(items), dash._iptr(o),
+             dash._iptr(t)) == dash.DASH_ERR_SHAPE
+    big = _lists(*dash.dash_schedule_table_family(sch.CAUSAL, 4, 2, dash.FAMILY_PACKED, 0, 1 << 30))
+    assert big == _lists(*dash.dash_schedule_table_family(sch.CAUSAL, 4, 2, dash.FAMILY_PACKED, 0, 8))
+    assert big == tuple(se.packed_table(sch.CAUSAL, 4, 2, 8))
+    assert len(big[0]) - 1 == 8
 
 
 def test_per_head_tables_on_256_key_tiles_only():
