@@ -230,6 +230,9 @@ namespace {
 // Simulation of any schedule given as a table (closed forms included).
 int run_problem(Problem& pb, const dash::GroupTable& tb, int dispatch, dash_sim_result* out) {
   if (!build(pb, tb)) return DASH_ERR_TABLE;
+  // workers beyond the items stay idle under either dispatch: keep no state
+  // for them (item k runs on worker k either way)
+  pb.P = std::min(pb.P, std::max(1, (int)pb.item_first.size() - 1));
   const int P = pb.P;
   std::vector<int> assign;
   double replay_mk = 0.0;

@@ -472,3 +472,18 @@ def test_bench_searched_table_row(monkeypatch):
             assert t["items"] == 64
         else:
             assert not t["per_head"]
+
+
+def test_sim_workers_beyond_the_items():
+    # more workers than items: the same result as one worker per item, for
+    # closed forms and tables, and no state kept for the idle workers
+    for m, s, N, G, groups in ((sch.CAUSAL, dash.SYMMETRIC_SHIFT, 8, 2, 3), (sch.FULL, dash.SHIFT, 6, 1, 2)):
+        items = groups * dash.dash_schedule_num_items(m, s, N)
+        for disp in (0, 1):
+            a = dash.dash_sim_run(m, s, N, G, groups, items, disp, 1.0, 0.5, 0.125)
+            b = dash.dash_sim_run(m, s, N, G, groups, 1 << 30, disp, 1.0, 0.5, 0.125)
+            assert a == b
+    offs, tasks = dash.dash_schedule_table_closed_form(sch.CAUSAL, dash.SHIFT, 8, 2)
+    a = dash.dash_sim_table(sch.CAUSAL, 8, 2, 3, 24, 1, offs, tasks, 1.0, 0.5, 0.125)
+    b = dash.dash_sim_table(sch.CAUSAL, 8, 2, 3, 1 << 30, 1, offs, tasks, 1.0, 0.5, 0.125)
+    assert a == b
