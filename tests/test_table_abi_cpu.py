@@ -228,6 +228,30 @@ def test_bwd_table_validation_before_device():
                                         1 << 30, None) == dash.DASH_ERR_SCHEDULE_MASK
 
 
+def _bwd_table_run(**kw):
+    args = dict(B=1, Hq=2, Hkv=1, S=1024, D=128, mask=0, table=1 << 12, tb=1 << 20, items=4,
+                grid=0, ws=1 << 12, wsb=1 << 30, q=1 << 12, dq=1 << 12)
+    args.update(kw)
+    p = ctypes.c_void_p
+    a = p(1 << 12)
+    return dash.lib().dash_attn_bwd_table_run(
+        p(args["q"]), a, a, a, p(args["dq"]), a, a, args["B"], args["Hq"], args["Hkv"], args["S"],
+        args["D"], args["mask"], p(args["table"]), args["tb"], args["items"], args["grid"],
+        p(args["ws"]), args["wsb"], None)
+
+
+def test_bwd_table_run_validation_before_device():
+    # the run phase alone checks like the one-call form (no o, lse needed)
+    assert _bwd_table_run(table=None) == dash.DASH_ERR_NULL
+    assert _bwd_table_run(table=(1 << 12) + 2) == dash.DASH_ERR_SHAPE
+    assert _bwd_table_run(items=0) == dash.DASH_ERR_TABLE
+    assert _bwd_table_run(items=9) == dash.DASH_ERR_TABLE
+    assert _bwd_table_run(tb=64) == dash.DASH_ERR_TABLE
+    assert _bwd_table_run(Hq=3, Hkv=2) == dash.DASH_ERR_SHAPE
+    assert _bwd_table_run(D=96) == dash.DASH_ERR_UNSUPPORTED
+    assert _bwd_table_run(S=0, table=None) == dash.DASH_OK
+
+
 def test_table_workspace_holds_per_head_partials():
     # with 256-key tiles and grouped heads a table may be in the per-head
     # form: the workspace keeps one fp32 dK/dV partial per query head, the
