@@ -173,7 +173,7 @@ struct LaneOffs {
   // constant parts of the dS write address of element x (see wr)
   static constexpr int wx(int x) {
     return T == 128 ? ((((x & 3) << 1) ^ ((x & 3) << 2) ^ (2 * (x >> 2))) << 4)
-                    : ((8 * (x & 1) ^ 6 * ((x >> 1) & 1) ^ ((x >> 2) & 1)) << 4);
+                    : ((8 * (x & 1) ^ 6 * ((x >> 1) & 1) ^ 3 * ((x >> 2) & 1)) << 4);
   }
   static constexpr int wy(int x) {
     return T == 128 ? (8 * (x >> 2) + (x & 3)) * 256 : (4 * (x >> 2) + ((x >> 1) & 1)) * 256;

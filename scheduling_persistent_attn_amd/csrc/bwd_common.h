@@ -33,7 +33,8 @@ __device__ __forceinline__ bf16x8 zero8() {
 // ---------------------------------------------------------------------------
 // LDS tiles use the swizzled layout of lds_layout.h: 16-byte row reads of one
 // column in 16 consecutive rows and the transposing 8-byte reads of 4 rows x
-// 64 bytes are both free of bank conflicts.
+// 64 bytes, or of two 4-row groups 8 rows apart x 32 bytes, are free of bank
+// conflicts.
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;

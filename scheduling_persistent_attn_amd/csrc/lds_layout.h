@@ -6,19 +6,23 @@
 // slot U of super-row R sits at slot U ^ sw(R).  The LDS of gfx950 serves
 // 256 bytes per cycle from 64 four-byte banks; with
 //   sw(R) = ((a << 1) ^ (a << 2)) ^ b,  a = R & 3,
-//   b = (R >> 2) & 3 for 256-byte rows, (R >> 2) & 1 for 128-byte rows,
-// two access shapes are free of bank conflicts: 16-byte reads of one column
-// in 16 consecutive rows, and the transposing 8-byte reads
-// (ds_read_b64_tr_b16) of 4 consecutive rows x 64 bytes.  sw depends only on
-// the low bits of the row, so moving by 16 rows is a constant offset, and
-// moving a slot index by a multiple of 2 (a 32-byte step) is an XOR.
+//   b = (R >> 2) & 3 for 256-byte rows, 3 * ((R >> 2) & 1) for 128-byte rows,
+// three access shapes are free of bank conflicts: 16-byte reads of one
+// column in 16 consecutive rows, the transposing 8-byte reads
+// (ds_read_b64_tr_b16) of 4 consecutive rows x 64 bytes, and those of two
+// 4-row groups 8 rows apart x 32 bytes (each 32 lanes of such a read cover
+// all 64 banks once).  For 128-byte rows the last shape is why b moves slot
+// bits 0 and 1: with bit 0 alone, super-rows R and R ^ 4 fall on the same
+// banks there.  sw depends only on the low bits of the row, so moving by 16
+// rows is a constant offset, and moving a slot index by a multiple of 2 (a
+// 32-byte step) is an XOR.
 #pragma once
 
 namespace dash {
 
 __device__ __forceinline__ int lds_sw16(int R, int row_bytes) {
   const int a = R & 3;
-  const int b = row_bytes == 256 ? ((R >> 2) & 3) : ((R >> 2) & 1);
+  const int b = row_bytes == 256 ? ((R >> 2) & 3) : 3 * ((R >> 2) & 1);
   return ((a << 1) ^ (a << 2)) ^ b;
 }
 
